@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark: grouped block-scaled quantization of a Qwen3-235B-A22B-shaped MoE
+layer on one MI355X.
+
+One step quantizes one layer (128 experts of gate_up bf16 [3072,4096] and 128
+of down bf16 [4096,1536], N(0, 0.015^2) with 1e-4 of entries x50) held in a
+reused stacking buffer: MXFP8 and NVFP4, each with linear and with swizzled
+scales, 16 experts per launch (64 launches per step).  Inputs are resident in
+HBM before timing starts.  The value is whole-step algorithmic bytes (bf16 in
++ payload + scales + per-expert encode scales) over wall time.
+
+Also reported: per-kernel HIP-event durations and the roofline of the
+dominant kernel, the CPU oracle on a bounded sample of the same workload,
+and secondary workloads (Qwen3-30B-A3B layer grouped vs per-expert launch,
+the [8192,7168] routed-activation split, the residual+RMSNorm+quant sweep,
+the small grouped case, a device copy as attainable-bandwidth reference).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--cpu-experts", type=int, default=16,
+                    help="gate_up experts in the CPU oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the grouped quantization shards by expert with no exchange; "
+              "run it per GPU with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_quantization_moe_amd as mxq
+    from nvfp4_quantization_moe_amd import workloads
+
+    mxq.lib()  # fail loudly without the built library
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    E, G = workloads.N_EXPERTS, workloads.GROUP
+    shapes = workloads.QWEN3_235B_A22B
+    log(f"[bench] generating one layer: {E} x gate_up {shapes['gate_up']} + {E} x down "
+        f"{shapes['down']} bf16")
+    buf = {p: workloads.expert_stack(E, r, c, std=0.015, seed=5000 + k, device=dev)
+           for k, (p, (r, c)) in enumerate(shapes.items())}
+    gsc = {p: workloads.encode_scale_from_amax(buf[p].float().abs().amax(dim=(1, 2))).contiguous()
+           for p in buf}
+    torch.cuda.synchronize()
+
+    # outputs: one payload buffer per format (both layouts write the same
+    # payload bytes), one scale buffer per (format, layout)
+    calls = []  # (fmt, layout, proj, GroupedCall)
+    alg_bytes = {}
+    for fmt in (mxq.MXFP8, mxq.NVFP4):
+        for proj, (r, c) in shapes.items():
+            pw = c if fmt == mxq.MXFP8 else c // 2
+            pay = torch.empty(E, r, pw, dtype=torch.uint8, device=dev)
+            for layout in (mxq.LINEAR, mxq.SWIZZLED):
+                nsc = mxq.scale_bytes(r, c, fmt, layout)
+                sc = torch.empty(E, nsc, dtype=torch.uint8, device=dev)
+                for b in range(0, E, G):
+                    srcs = [buf[proj][b + i] for i in range(G)]
+                    gs = gsc[proj][b:b + G] if fmt == mxq.NVFP4 else None
+                    call = mxq.GroupedCall(fmt, layout, srcs, [pay[b + i] for i in range(G)],
+                                           [sc[b + i] for i in range(G)], gs)
+                    nbytes = G * (r * c * 2 + r * pw + nsc + (4 if fmt == mxq.NVFP4 else 0))
+                    calls.append((fmt, layout, proj, call, nbytes))
+                    alg_bytes[(fmt, layout)] = alg_bytes.get((fmt, layout), 0) + nbytes
+    step_bytes = sum(c[4] for c in calls)
+
+    def step(events=None):
+        for k, (fmt, layout, proj, call, nb) in enumerate(calls):
+            if events is not None:
+                events[k][0].record()
+            call()
+            if events is not None:
+                events[k][1].record()
+
+    log(f"[bench] warmup {args.warmup} steps ({len(calls)} launches/step)")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in calls] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = step_bytes * args.steps / elapsed / 1e9
+
+    # per-kernel durations from the events
+    names = {(0, 0): "k_grouped<MXFP8,LINEAR>", (0, 1): "k_grouped<MXFP8,SWIZZLED>",
+             (1, 0): "k_grouped<NVFP4,LINEAR>", (1, 1): "k_grouped<NVFP4,SWIZZLED>"}
+    per = {}
+    for s in range(args.steps):
+        for k, (fmt, layout, proj, call, nb) in enumerate(calls):
+            ms = evs[s][k][0].elapsed_time(evs[s][k][1])
+            d = per.setdefault((fmt, layout), {"ms": 0.0, "n": 0, "bytes": 0})
+            d["ms"] += ms
+            d["n"] += 1
+            d["bytes"] += nb
+    per_kernel = {}
+    for key, d in per.items():
+        avg_us = d["ms"] * 1e3 / d["n"]
+        gbs = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        per_kernel[names[key]] = {"launches": d["n"], "avg_us": round(avg_us, 2),
+                                  "alg_bytes_per_launch": d["bytes"] // d["n"],
+                                  "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(per, key=lambda k: per[k]["ms"])
+    dd = per[dom]
+    achieved = dd["bytes"] / (dd["ms"] * 1e-3) / 1e9
+    roofline = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "alg_bytes_per_launch": dd["bytes"] // dd["n"],
+                "avg_launch_us": round(dd["ms"] * 1e3 / dd["n"], 2)}
+    log(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} GB/s; dominant {names[dom]} "
+        f"{achieved:.1f} GB/s")
+
+    out = {
+        "metric": "effective HBM GB/s (bytes in+out) and % of HBM peak, grouped expert quant",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "config": {
+            "workload": "Qwen3-235B-A22B-shaped MoE layer: 128 experts gate_up bf16 [3072,4096] "
+                        "+ 128 down bf16 [4096,1536], N(0,0.015^2) with 1e-4 outliers x50; "
+                        "MXFP8 and NVFP4, linear and swizzled scales, 16 experts per launch",
+            "experts": E, "experts_per_launch": G, "launches_per_step": len(calls),
+            "alg_bytes_per_step": step_bytes,
+            "alg_bytes_per_layer": {"mxfp8": alg_bytes[(0, 0)], "nvfp4": alg_bytes[(1, 0)]},
+        },
+        "per_kernel": per_kernel,
+        "roofline": roofline,
+    }
+
+    if not args.no_extra:
+        out["other_workloads"] = extra_workloads(torch, mxq, workloads, dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(torch, buf["gate_up"], args.cpu_experts)
+    print(json.dumps(out), flush=True)
+
+
+def timed(torch, fn, iters, warm=3):
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters * 1e-3  # seconds per iteration
+
+
+def extra_workloads(torch, mxq, workloads, dev):
+    res = {}
+    # attainable-bandwidth reference: a 4 GiB device copy (read + write)
+    n = 1 << 31
+    a = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    t = timed(torch, lambda i: b.copy_(a), 10)
+    res["d2d_copy_4GiB"] = {"GBps": round(2 * n * 2 / t / 1e9, 1)}
+    del a, b
+
+    # Qwen3-30B-A3B layer, MXFP8 swizzled: 16 grouped launches vs 256 per-expert launches
+    E, G = workloads.N_EXPERTS, workloads.GROUP
+    layer = {p: workloads.expert_stack(E, r, c, std=0.02, seed=2000, device=dev)
+             for p, (r, c) in workloads.QWEN3_30B_A3B.items()}
+    grouped, single = [], []
+    nbytes = 0
+    for p, (r, c) in workloads.QWEN3_30B_A3B.items():
+        pay = torch.empty(E, r, c, dtype=torch.uint8, device=dev)
+        sc = torch.empty(E, mxq.scale_bytes(r, c, 0, 1), dtype=torch.uint8, device=dev)
+        nbytes += E * (r * c * 3 + sc.shape[1])
+        for b0 in range(0, E, G):
+            grouped.append(mxq.GroupedCall(0, 1, [layer[p][b0 + i] for i in range(G)],
+                                           [pay[b0 + i] for i in range(G)],
+                                           [sc[b0 + i] for i in range(G)]))
+        for i in range(E):
+            single.append(mxq.GroupedCall(0, 1, [layer[p][i]], [pay[i]], [sc[i]]))
+    tg = timed(torch, lambda i: [c() for c in grouped], 10)
+    ts = timed(torch, lambda i: [c() for c in single], 10)
+    res["qwen3_30b_a3b_layer_mxfp8_swizzled"] = {
+        "alg_bytes": nbytes,
+        "grouped_16_launches_us": round(tg * 1e6, 1), "grouped_GBps": round(nbytes / tg / 1e9, 1),
+        "per_expert_256_launches_us": round(ts * 1e6, 1),
+        "per_expert_GBps": round(nbytes / ts / 1e9, 1),
+        "overhead_per_extra_launch_us": round((ts - tg) / (len(single) - len(grouped)) * 1e6, 2)}
+    del layer, grouped, single
+
+    # routed activation split, NVFP4 swizzled, 8 rotating input copies (> MALL)
+    x, split = workloads.routed_activation()
+    xs = [x.to(dev) for _ in range(8)]
+    g = workloads.encode_scale_from_amax(xs[0].float().abs().amax()).reshape(1)
+    T, H = x.shape
+    total = mxq.split_scale_offset(split, len(split), H)
+    pay = torch.empty(T, H // 2, dtype=torch.uint8, device=dev)
+    sc = torch.empty(total, dtype=torch.uint8, device=dev)
+    am = torch.empty(T, dtype=torch.float32, device=dev)
+    t = timed(torch, lambda i: mxq.nvfp4_quant_split(xs[i % 8], split, g, 1, pay, sc, am), 20)
+    nb = T * H * 2 + T * H // 2 + total + 4 * T + 4
+    res["split_nvfp4_8192x7168_256experts"] = {"us": round(t * 1e6, 1), "alg_bytes": nb,
+                                                "GBps": round(nb / t / 1e9, 1)}
+    del xs
+
+    # fused residual + RMSNorm + MXFP8 (swizzled), with the same-run e4m3 cast reference
+    sweep = {}
+    for T in (1, 16, 64, 256, 1024, 4096):
+        H = 7168
+        ins = [workloads.epilogue_inputs(T, H, seed=4000 + T + k, device=dev) for k in range(4)]
+        nsc = mxq.scale_bytes(T, H, 0, 1)
+        outs = (torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                torch.empty(T, H, dtype=torch.uint8, device=dev),
+                torch.empty(nsc, dtype=torch.uint8, device=dev))
+        t = timed(torch, lambda i: mxq.rmsnorm_quant_fused(*ins[i % 4], 1e-6, 0, 1, out=outs), 50)
+        tc = timed(torch, lambda i: ins[i % 4][0].to(torch.float8_e4m3fn), 50)
+        nb = T * H * 9 + nsc + 2 * H
+        sweep[str(T)] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1),
+                         "e4m3_cast_us": round(tc * 1e6, 2)}
+    res["fused_rmsnorm_mxfp8_H7168"] = sweep
+
+    # small grouped case: 8 x [256,512] MXFP8 linear (launch-bound)
+    xs8 = [x.to(dev) for x in workloads.small_grouped_experts(seed=0)]
+    call = mxq.GroupedCall(0, 0, xs8)
+    t = timed(torch, lambda i: call(), 100)
+    res["small_grouped_8x256x512_mxfp8"] = {"us": round(t * 1e6, 2),
+                                            "GBps": round(3178496 / t / 1e9, 1)}
+    return res
+
+
+def cpu_baseline(torch, gate_up, n_experts):
+    """The oracle, single-threaded, on the first n_experts gate_up experts
+    (MXFP8, swizzled): the same input bytes the GPU quantized."""
+    import numpy as np
+    import oracle
+    oracle.lib()
+    host = gate_up[:n_experts].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    rows, cols = host.shape[1], host.shape[2]
+    t0 = time.perf_counter()
+    for i in range(n_experts):
+        oracle.quantize(oracle.MXFP8, oracle.SWIZZLED, host[i])
+    dt = time.perf_counter() - t0
+    nb = n_experts * (rows * cols * 3 + rows * cols // 32)
+    return {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_experts} gate_up experts bf16 [{rows},{cols}] of the same layer, "
+                      f"MXFP8 with swizzled scales ({nb} algorithmic bytes, {dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

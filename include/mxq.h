@@ -1,0 +1,186 @@
+/*
+ * mxq.h -- C ABI of the MI355X (gfx950) block-scaled quantization library
+ * for Mixture-of-Experts tensors: MXFP8 and NVFP4, grouped over experts or
+ * split per expert, with linear or swizzled 128x4 scale layouts, and a fused
+ * residual-add + RMSNorm + quantize epilogue.
+ *
+ * Pages the operations come from (cited by title and section):
+ *   [RL-3804]   NVIDIA-NeMo/RL #3804 "perf(refit): batch MXFP8 expert
+ *               prequantization" (Summary; Why; Self-review > Verified clean)
+ *   [MO-2750]   NVIDIA/Model-Optimizer #2750 "Fold fused experts' quantizers
+ *               into their weights shard-locally" (commits; review)
+ *   [TRT-17452] NVIDIA/TensorRT-LLM #17452 "NVFP4 linear-SF AllReduce
+ *               epilogue" (layout, fold and exactness-test commits)
+ *   [TE-3800]   NVIDIA/TransformerEngine #3800, split quantization of
+ *               row-scaled NVFP4 activations (Description; Changes; diagram)
+ *   [TRT-17453] NVIDIA/TensorRT-LLM #17453 "MXFP8 carrier and quantize
+ *               folds" (Triton func, merge kernel, invariance-test and
+ *               AllReduce-epilogue commits)
+ *
+ * Formats.  Input elements are bf16.  MXFP8: blocks of 32 contiguous row
+ * elements, one E8M0 scale byte per block (code c means 2^(c-127); c is the
+ * smallest code with amax <= 448 * 2^(c-127)), E4M3 elements (OCP, largest
+ * finite 448, round to nearest even, sign of zero kept; the reciprocal of the
+ * block scale is flushed to zero when the scale or the reciprocal is not a
+ * normal fp32 number).  NVFP4: blocks of 16, one E4M3 scale byte per block
+ * under an fp32 encode scale g (block scale s = fp32(fp32(amax/6) * g)
+ * rounded to E4M3 with saturation; element multiplier fp32(g / s_q)), E2M1
+ * elements saturating at 6, two per byte, element 2j in the low nibble of
+ * byte j.  Results are bit-identical to the definitions above, whatever the
+ * grouping, split or launch shape.
+ *
+ * Scale layouts [TRT-17452, layout commit; TRT-17453, AllReduce epilogue
+ * commit].  LINEAR: byte (r, c) of an [R, C] scale matrix at r*C + c.
+ * SWIZZLED_128x4: rows padded to a multiple of 128, columns to a multiple of
+ * 4; each 128x4 tile is 512 contiguous bytes, tiles in row-tile-major order;
+ * inside a tile (r, c) is at (r%32)*16 + ((r%128)/32)*4 + c%4.  Every padding
+ * byte is written as 0, so scale buffers need no prior zeroing
+ * [TRT-17453, merge-kernel commit].
+ *
+ * Ownership and streams.  The caller owns every buffer; the library keeps no
+ * allocation, stream, cache or mutable state other than the debug grid cap
+ * below.  Pointers marked "device" are device memory; everything else is host
+ * memory read during the call only.  All GPU work is enqueued on `stream`
+ * (a hipStream_t; NULL is the null stream) and the call returns without
+ * synchronizing; the caller makes the inputs ready on that stream.  No call
+ * allocates, copies or synchronizes, so every call may be captured in a HIP
+ * graph.  Outputs must not alias inputs or each other.
+ *
+ * Errors.  Every call validates all arguments on the host first; on any error
+ * it returns a nonzero mxq_status, launches nothing and writes nothing.
+ * MXQ_ELAUNCH reports a failed kernel launch.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_EINVAL = 1,       /* null pointer, bad enum, bad count or split, bad eps       */
+    MXQ_ESHAPE = 2,       /* cols not a multiple of the block, misaligned pointer ... */
+    MXQ_EUNSUPPORTED = 3, /* a combination this build does not implement            */
+    MXQ_ELAUNCH = 4       /* the HIP runtime rejected a kernel launch                 */
+} mxq_status;
+
+typedef enum { MXQ_MXFP8 = 0, MXQ_NVFP4 = 1 } mxq_format;
+typedef enum { MXQ_SF_LINEAR = 0, MXQ_SF_SWIZZLED = 1 } mxq_sf_layout;
+
+#define MXQ_MAX_GROUP 16 /* experts per grouped call [RL-3804, Summary] */
+
+/* One expert tensor of a grouped call. */
+typedef struct {
+    const void *src;          /* device bf16 [rows, src_ld], 16-byte aligned; the
+                                 first `cols` elements of each row are read     */
+    void *payload;            /* device u8, dense: MXFP8 [rows, cols], NVFP4
+                                 [rows, cols/2]; 16-byte aligned                 */
+    void *scales;             /* device u8, mxq_scale_bytes(rows, cols, fmt,
+                                 layout) bytes; 16-byte aligned if swizzled     */
+    const float *global_scale;/* device fp32 scalar: NVFP4 encode scale g
+                                 (finite, > 0, <= 2^100); ignored for MXFP8     */
+    int64_t rows;             /* >= 0 and < 2^31; 0 writes nothing             */
+    int64_t src_ld;           /* row stride in elements: >= cols, multiple of 8 */
+} mxq_entry;
+
+/*
+ * mx_quant_grouped -- quantize 1..16 expert tensors that share `cols` in ONE
+ * kernel launch driven by a descriptor table [RL-3804, Summary; Why;
+ * Self-review > Verified clean: batched quantization is bit-identical to the
+ * per-tensor path because the format is row-independent; a per-call cap of
+ * 16, where one entry is exactly the per-expert path].
+ *   fmt, layout  mxq_format, mxq_sf_layout
+ *   cols         elements per row; a multiple of 32 (MXFP8) or 16 (NVFP4),
+ *                at most 32768 (MXFP8) or 16384 (NVFP4)
+ *   entries      host array of n_entries descriptors; each entry's rows may
+ *                differ
+ * Returns MXQ_EINVAL for n_entries outside [1, 16], a null pointer or a bad
+ * enum; MXQ_ESHAPE for a bad cols, src_ld or alignment.
+ */
+int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries, int n_entries,
+                     void *stream);
+
+/*
+ * nvfp4_quant_split -- quantize a concatenated routed activation once and
+ * split it per expert [TE-3800, Description; Changes: independent per-expert
+ * scale padding including uneven and empty splits; requantizing one expert
+ * does not modify another expert's storage; diagram: split packed values and
+ * row amax, split scales with separate expert padding].
+ *   src          device bf16 [total_rows, cols], contiguous, 16-byte aligned
+ *   split_rows   host int64[n_splits], each >= 0, summing to total_rows;
+ *                expert i owns rows [o_i, o_i + m_i), o_i = sum_{j<i} m_j
+ *   global_scale device fp32 scalar g shared by all rows (as for entries)
+ *   payload      device u8 [total_rows, cols/2]; expert i's rows are rows
+ *                [o_i, o_i + m_i) (16-byte aligned base)
+ *   scales       device u8 bulk buffer; expert i's scale matrix [m_i, cols/16]
+ *                in `layout` starts at mxq_split_scale_offset(..., i, ...) and
+ *                holds mxq_scale_bytes(m_i, cols, MXQ_NVFP4, layout) bytes:
+ *                swizzled pads each expert to a multiple of 128 rows; an empty
+ *                expert owns no bytes (16-byte aligned base if swizzled)
+ *   row_amax     device fp32 [total_rows]: max_j |src[r, j]| (NULL to skip)
+ * cols is a multiple of 16, at most 16384.  Any number of splits is allowed.
+ * total_rows == 0 is MXQ_OK with no launch.
+ */
+int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols,
+                      const int64_t *split_rows, int n_splits, const float *global_scale,
+                      void *payload, void *scales, float *row_amax, int layout, void *stream);
+
+/*
+ * rmsnorm_quant_fused -- residual add + RMSNorm + block quantization in one
+ * pass [TRT-17452, fold commit: the epilogue quantizes the same bf16 values
+ * it writes to norm_out; TRT-17453, AllReduce epilogue commit: bitwise equal
+ * to quantizing norm_out afterwards, the invented scale rows past the last
+ * live row are zeroed by the kernel, a hidden size that would pad scale
+ * columns is rejected on the host].  Single GPU; no collective.
+ *   x, residual  device bf16 [T, H]; gamma device bf16 [H]
+ *   residual_out device bf16 [T, H] = bf16(x + residual)
+ *   norm_out     device bf16 [T, H] = bf16(r * gamma / sqrt(mean(r^2) + eps)),
+ *                fp32 arithmetic (within 1 bf16 ulp of the exact value)
+ *   payload, scales  fmt/layout quantization of norm_out (as mx_quant_grouped
+ *                with rows = T, cols = H); swizzled scale rows T..round_up(T,128)
+ *                are written as zero
+ *   global_scale device fp32 g for NVFP4; ignored for MXFP8
+ * H is a multiple of 32 (MXFP8) or 16 (NVFP4) and at most 16384; with the
+ * swizzled layout H must also give a multiple of 4 scale columns (H % 128 == 0
+ * for MXFP8, H % 64 == 0 for NVFP4), else MXQ_ESHAPE.  eps must be finite and
+ * > 0.  T == 0 is MXQ_OK with no launch.  All pointers 16-byte aligned.
+ */
+int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual,
+                        const void *gamma, float eps, int64_t T, int64_t H,
+                        const float *global_scale, void *residual_out, void *norm_out,
+                        void *payload, void *scales, void *stream);
+
+/*
+ * scale_swizzle -- convert a linear [rows, sf_cols] scale matrix to the
+ * swizzled 128x4 layout, zero padded [RL-3804, Summary: receiver-side layout
+ * conversion; TRT-17453, invariance-test commit: the two layouts agree].
+ *   linear    device u8 [rows, sf_cols]
+ *   swizzled  device u8 [round_up(rows,128) * round_up(sf_cols,4)], 16-byte
+ *             aligned
+ */
+int scale_swizzle(const void *linear, int64_t rows, int64_t sf_cols, void *swizzled,
+                  void *stream);
+
+/* Size of one scale matrix for a [rows, cols] tensor; -1 on bad arguments. */
+int64_t mxq_scale_bytes(int64_t rows, int64_t cols, int fmt, int layout);
+
+/* Byte offset of split i's scales in the bulk buffer (i == n_splits gives the
+ * total size); -1 on bad arguments. */
+int64_t mxq_split_scale_offset(const int64_t *split_rows, int n_splits, int i, int64_t cols,
+                               int fmt, int layout);
+
+/* Static description of a status code. */
+const char *mxq_status_str(int status);
+
+/* Debug and test knob: cap the number of workgroups a launch may use
+ * (0 restores the default).  Outputs do not depend on it; the tests use it to
+ * show that.  Process-wide; not thread-safe. */
+void mxq_set_max_workgroups(int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXQ_H */

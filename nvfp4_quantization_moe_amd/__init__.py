@@ -1,0 +1,303 @@
+"""MI355X-native block-scaled (MXFP8 / NVFP4) quantization of MoE expert tensors.
+
+Thin Python binding over the C ABI of ``libmxq.so`` (declared in
+``include/mxq.h``).  PyTorch supplies device memory and the current HIP
+stream; every quantization step runs in the library's HIP kernels.  The
+binding only checks tensor metadata, allocates outputs when the caller does
+not pass them, and forwards pointers.  There is no CPU fallback: without the
+built library, or without GPU tensors, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+__all__ = [
+    "MXFP8", "NVFP4", "LINEAR", "SWIZZLED", "MAX_GROUP", "MxqError",
+    "mx_quant_grouped", "nvfp4_quant_split", "rmsnorm_quant_fused", "scale_swizzle",
+    "GroupedCall", "scale_bytes", "split_scale_offset", "set_max_workgroups", "library_path", "lib",
+]
+
+MXFP8, NVFP4 = 0, 1
+LINEAR, SWIZZLED = 0, 1
+MAX_GROUP = 16
+_BLOCK = {MXFP8: 32, NVFP4: 16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmxq.so")
+_lib = None
+
+
+class MxqError(RuntimeError):
+    pass
+
+
+class _Entry(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("payload", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("global_scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("src_ld", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MxqError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m nvfp4_quantization_moe_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, vp, ci, cf = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        sigs = {
+            "mx_quant_grouped": (ci, [ci, ci, i64, ctypes.POINTER(_Entry), ci, vp]),
+            "nvfp4_quant_split": (ci, [vp, i64, i64, ctypes.POINTER(i64), ci, vp, vp, vp, vp,
+                                       ci, vp]),
+            "rmsnorm_quant_fused": (ci, [ci, ci, vp, vp, vp, cf, i64, i64, vp, vp, vp, vp, vp,
+                                         vp]),
+            "scale_swizzle": (ci, [vp, i64, i64, vp, vp]),
+            "mxq_scale_bytes": (i64, [i64, i64, ci, ci]),
+            "mxq_split_scale_offset": (i64, [ctypes.POINTER(i64), ci, ci, i64, ci, ci]),
+            "mxq_status_str": (ctypes.c_char_p, [ci]),
+            "mxq_set_max_workgroups": (None, [i64]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc == 0:
+        return
+    msg = f"{what}: {lib().mxq_status_str(rc).decode()} (status {rc})"
+    if rc in (1, 2):
+        raise ValueError(msg)
+    if rc == 3:
+        raise NotImplementedError(msg)
+    raise MxqError(msg)
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_gpu(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def scale_bytes(rows: int, cols: int, fmt: int, layout: int) -> int:
+    n = lib().mxq_scale_bytes(rows, cols, fmt, layout)
+    if n < 0:
+        raise ValueError("scale_bytes: invalid arguments")
+    return n
+
+
+def split_scale_offset(split_rows: Sequence[int], i: int, cols: int, fmt: int = NVFP4,
+                       layout: int = SWIZZLED) -> int:
+    arr = (ctypes.c_int64 * max(len(split_rows), 1))(*split_rows)
+    n = lib().mxq_split_scale_offset(arr, len(split_rows), i, cols, fmt, layout)
+    if n < 0:
+        raise ValueError("split_scale_offset: invalid arguments")
+    return n
+
+
+def set_max_workgroups(n: int) -> None:
+    """Debug knob: cap workgroups per launch (0 = default).  Outputs do not change."""
+    lib().mxq_set_max_workgroups(int(n))
+
+
+def mx_quant_grouped(fmt: int, layout: int, srcs: Sequence[torch.Tensor],
+                     payloads: Optional[Sequence[torch.Tensor]] = None,
+                     scales: Optional[Sequence[torch.Tensor]] = None,
+                     global_scales: Optional[torch.Tensor] = None):
+    """Quantize same-width bf16 expert tensors, MAX_GROUP per launch.
+
+    srcs: 2-D bf16 GPU tensors [rows_i, cols] with unit column stride.
+    global_scales: NVFP4 only, fp32 GPU tensor [len(srcs)] of encode scales.
+    Returns (payloads, scales) lists of uint8 tensors (allocated when None):
+    payload [rows, cols] (MXFP8) or [rows, cols/2] (NVFP4); scales flat,
+    scale_bytes(rows, cols, fmt, layout) bytes."""
+    srcs = list(srcs)
+    if not srcs:
+        return [], []
+    payloads, scales = _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales)
+    cols = srcs[0].shape[1]
+    dev = srcs[0].device
+    stream = _stream(dev)
+    for b in range(0, len(srcs), MAX_GROUP):
+        n = min(MAX_GROUP, len(srcs) - b)
+        ents = (_Entry * n)()
+        for j in range(n):
+            i = b + j
+            s = srcs[i]
+            gs = None if fmt == MXFP8 else global_scales.data_ptr() + 4 * i
+            ents[j] = _Entry(s.data_ptr(), payloads[i].data_ptr(), scales[i].data_ptr(), gs,
+                             s.shape[0], s.stride(0))
+        _check(lib().mx_quant_grouped(fmt, layout, cols, ents, n, stream), "mx_quant_grouped")
+    return payloads, scales
+
+
+class GroupedCall:
+    """mx_quant_grouped with its descriptor tables built once.
+
+    For callers that issue the same grouped quantization repeatedly (a refit
+    loop, a benchmark): the tensors are checked and the C descriptor arrays
+    packed at construction; each call is one C call per 16 experts on the
+    current stream.  The tensors must stay alive and keep their storage."""
+
+    def __init__(self, fmt, layout, srcs, payloads=None, scales=None, global_scales=None):
+        self.fmt, self.layout = fmt, layout
+        self.payloads, self.scales = _grouped_outputs(fmt, layout, srcs, payloads, scales,
+                                                      global_scales)
+        self.srcs = list(srcs)
+        self.global_scales = global_scales
+        self.cols = self.srcs[0].shape[1]
+        self.device = self.srcs[0].device
+        self._batches = []
+        for b in range(0, len(self.srcs), MAX_GROUP):
+            n = min(MAX_GROUP, len(self.srcs) - b)
+            ents = (_Entry * n)()
+            for j in range(n):
+                i = b + j
+                s = self.srcs[i]
+                gs = None if fmt == MXFP8 else global_scales.data_ptr() + 4 * i
+                ents[j] = _Entry(s.data_ptr(), self.payloads[i].data_ptr(),
+                                 self.scales[i].data_ptr(), gs, s.shape[0], s.stride(0))
+            self._batches.append((ents, n))
+
+    def __call__(self, stream: Optional[ctypes.c_void_p] = None):
+        stream = _stream(self.device) if stream is None else stream
+        L = lib()
+        for ents, n in self._batches:
+            _check(L.mx_quant_grouped(self.fmt, self.layout, self.cols, ents, n, stream),
+                   "mx_quant_grouped")
+        return self.payloads, self.scales
+
+
+def _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales):
+    srcs = list(srcs)
+    cols = srcs[0].shape[-1]
+    dev = srcs[0].device
+    for i, s in enumerate(srcs):
+        _need_gpu(s, f"srcs[{i}]", torch.bfloat16)
+        if s.dim() != 2 or s.stride(1) != 1 or s.shape[1] != cols or s.device != dev:
+            raise ValueError(f"srcs[{i}]: expected a row-major [rows, {cols}] bf16 tensor on {dev}")
+    if fmt == NVFP4:
+        if global_scales is None:
+            raise ValueError("NVFP4 needs global_scales")
+        _need_gpu(global_scales, "global_scales", torch.float32)
+        if global_scales.numel() != len(srcs) or not global_scales.is_contiguous():
+            raise ValueError("global_scales must be a contiguous fp32 tensor with one value per src")
+    pw = cols if fmt == MXFP8 else cols // 2
+    if payloads is None:
+        payloads = [torch.empty((s.shape[0], pw), dtype=torch.uint8, device=dev) for s in srcs]
+    if scales is None:
+        scales = [torch.empty(scale_bytes(s.shape[0], cols, fmt, layout), dtype=torch.uint8,
+                              device=dev) for s in srcs]
+    payloads, scales = list(payloads), list(scales)
+    for i, (s, p, c) in enumerate(zip(srcs, payloads, scales)):
+        _need_gpu(p, f"payloads[{i}]", torch.uint8)
+        _need_gpu(c, f"scales[{i}]", torch.uint8)
+        if p.numel() < s.shape[0] * pw or not p.is_contiguous():
+            raise ValueError(f"payloads[{i}] too small or not contiguous")
+        if c.numel() < scale_bytes(s.shape[0], cols, fmt, layout) or not c.is_contiguous():
+            raise ValueError(f"scales[{i}] too small or not contiguous")
+    return payloads, scales
+
+
+def nvfp4_quant_split(src: torch.Tensor, split_rows: Sequence[int], global_scale: torch.Tensor,
+                      layout: int = SWIZZLED, payload: Optional[torch.Tensor] = None,
+                      scales: Optional[torch.Tensor] = None,
+                      row_amax: Optional[torch.Tensor] = None, want_row_amax: bool = True):
+    """Quantize a concatenated bf16 activation [T, H] once and split it per
+    expert.  Returns (payload [T, H/2], bulk scales, row_amax [T] or None);
+    expert i's scales start at split_scale_offset(split_rows, i, H)."""
+    _need_gpu(src, "src", torch.bfloat16)
+    _need_gpu(global_scale, "global_scale", torch.float32)
+    if src.dim() != 2 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous [T, H] bf16 tensor")
+    T, H = src.shape
+    split_rows = [int(v) for v in split_rows]
+    dev = src.device
+    if payload is None:
+        payload = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        total = split_scale_offset(split_rows, len(split_rows), H, NVFP4, layout)
+        scales = torch.empty(total, dtype=torch.uint8, device=dev)
+    if row_amax is None and want_row_amax:
+        row_amax = torch.empty(T, dtype=torch.float32, device=dev)
+    _need_gpu(payload, "payload", torch.uint8)
+    _need_gpu(scales, "scales", torch.uint8)
+    if row_amax is not None:
+        _need_gpu(row_amax, "row_amax", torch.float32)
+    arr = (ctypes.c_int64 * max(len(split_rows), 1))(*split_rows)
+    rc = lib().nvfp4_quant_split(src.data_ptr(), T, H, arr, len(split_rows),
+                                 global_scale.data_ptr(), payload.data_ptr(), scales.data_ptr(),
+                                 _ptr(row_amax), layout, _stream(dev))
+    _check(rc, "nvfp4_quant_split")
+    return payload, scales, row_amax
+
+
+def rmsnorm_quant_fused(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                        eps: float = 1e-6, fmt: int = MXFP8, layout: int = SWIZZLED,
+                        global_scale: Optional[torch.Tensor] = None, out=None):
+    """residual_out = bf16(x + residual); norm_out = RMSNorm(residual_out) * gamma
+    (bf16); payload/scales = fmt quantization of norm_out.  Returns
+    (residual_out, norm_out, payload, scales)."""
+    _need_gpu(x, "x", torch.bfloat16)
+    _need_gpu(residual, "residual", torch.bfloat16)
+    _need_gpu(gamma, "gamma", torch.bfloat16)
+    if x.dim() != 2 or not x.is_contiguous() or residual.shape != x.shape or \
+            not residual.is_contiguous() or gamma.shape != (x.shape[1],) or not gamma.is_contiguous():
+        raise ValueError("x, residual: contiguous [T, H]; gamma: contiguous [H]")
+    T, H = x.shape
+    dev = x.device
+    if fmt == NVFP4:
+        if global_scale is None:
+            raise ValueError("NVFP4 needs global_scale")
+        _need_gpu(global_scale, "global_scale", torch.float32)
+    if out is None:
+        pw = H if fmt == MXFP8 else H // 2
+        nb = lib().mxq_scale_bytes(T, H, fmt, layout)
+        if nb < 0:
+            raise ValueError("rmsnorm_quant_fused: bad H for this format")
+        out = (torch.empty_like(x), torch.empty_like(x),
+               torch.empty((T, pw), dtype=torch.uint8, device=dev),
+               torch.empty(nb, dtype=torch.uint8, device=dev))
+    res_out, norm_out, payload, scales = out
+    rc = lib().rmsnorm_quant_fused(fmt, layout, x.data_ptr(), residual.data_ptr(),
+                                   gamma.data_ptr(), float(eps), T, H, _ptr(global_scale),
+                                   res_out.data_ptr(), norm_out.data_ptr(), payload.data_ptr(),
+                                   scales.data_ptr(), _stream(dev))
+    _check(rc, "rmsnorm_quant_fused")
+    return res_out, norm_out, payload, scales
+
+
+def scale_swizzle(linear: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Linear [rows, sf_cols] uint8 scales -> flat swizzled 128x4 layout."""
+    _need_gpu(linear, "linear", torch.uint8)
+    if linear.dim() != 2 or not linear.is_contiguous():
+        raise ValueError("linear must be a contiguous [rows, sf_cols] uint8 tensor")
+    rows, C = linear.shape
+    if out is None:
+        n = (-(-rows // 128) * 128) * (-(-C // 4) * 4)
+        out = torch.empty(n, dtype=torch.uint8, device=linear.device)
+    _need_gpu(out, "out", torch.uint8)
+    rc = lib().scale_swizzle(linear.data_ptr(), rows, C, out.data_ptr(), _stream(linear.device))
+    _check(rc, "scale_swizzle")
+    return out

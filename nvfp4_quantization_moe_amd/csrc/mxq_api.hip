@@ -1,0 +1,231 @@
+// mxq_api.hip -- the C ABI declared in include/mxq.h: argument validation,
+// descriptor-table packing and kernel launches.  Every check runs on the host
+// before any launch; a call that fails a check enqueues nothing.
+#include <stdint.h>
+#include <string.h>
+
+#include "mxq_internal.h"
+
+using namespace mxq;
+
+namespace {
+
+int64_t g_max_workgroups = 0;  // debug grid cap; 0 = one workgroup per unit
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline bool valid_fmt(int f) { return f == MXQ_MXFP8 || f == MXQ_NVFP4; }
+inline bool valid_layout(int l) { return l == MXQ_SF_LINEAR || l == MXQ_SF_SWIZZLED; }
+inline int64_t block_of(int fmt) { return fmt == MXQ_MXFP8 ? 32 : 16; }
+inline int64_t max_cols(int fmt) { return fmt == MXQ_MXFP8 ? kMaxColsMx : kMaxColsNv; }
+
+// Work units (32-row groups) for a tensor of `rows` rows.  Swizzled units
+// cover the padded rows too, so the padding is written by the kernel.
+inline int64_t units_for(int64_t rows, int layout) {
+    if (rows <= 0) return 0;
+    return layout == MXQ_SF_SWIZZLED ? round_up(rows, 128) / kUnitRows
+                                     : (rows + kUnitRows - 1) / kUnitRows;
+}
+
+inline int64_t grid_for(int64_t units) {
+    if (g_max_workgroups > 0 && g_max_workgroups < units) return g_max_workgroups;
+    return units;
+}
+
+inline int64_t sf_bytes(int64_t rows, int64_t C, int layout) {
+    if (layout == MXQ_SF_LINEAR) return rows * C;
+    return round_up(rows, 128) * round_up(C, 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mxq_status_str(int status) {
+    switch (status) {
+    case MXQ_OK: return "ok";
+    case MXQ_EINVAL: return "invalid argument (null pointer, enum, count, split or eps)";
+    case MXQ_ESHAPE: return "unsupported shape or alignment";
+    case MXQ_EUNSUPPORTED: return "combination not implemented";
+    case MXQ_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+void mxq_set_max_workgroups(int64_t n) { g_max_workgroups = n > 0 ? n : 0; }
+
+int64_t mxq_scale_bytes(int64_t rows, int64_t cols, int fmt, int layout) {
+    if (!valid_fmt(fmt) || !valid_layout(layout) || rows < 0 || cols <= 0 ||
+        cols % block_of(fmt) != 0)
+        return -1;
+    return sf_bytes(rows, cols / block_of(fmt), layout);
+}
+
+int64_t mxq_split_scale_offset(const int64_t *split_rows, int n_splits, int i, int64_t cols,
+                               int fmt, int layout) {
+    if (!split_rows || n_splits < 0 || i < 0 || i > n_splits) return -1;
+    if (!valid_fmt(fmt) || !valid_layout(layout) || cols <= 0 || cols % block_of(fmt) != 0)
+        return -1;
+    int64_t off = 0;
+    for (int j = 0; j < n_splits; ++j)
+        if (split_rows[j] < 0) return -1;
+    for (int j = 0; j < i; ++j) off += sf_bytes(split_rows[j], cols / block_of(fmt), layout);
+    return off;
+}
+
+int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries, int n_entries,
+                     void *stream) {
+    if (!valid_fmt(fmt) || !valid_layout(layout) || !entries || n_entries < 1 ||
+        n_entries > MXQ_MAX_GROUP)
+        return MXQ_EINVAL;
+    if (cols <= 0 || cols % block_of(fmt) != 0 || cols > max_cols(fmt)) return MXQ_ESHAPE;
+    GroupArgs a;
+    memset(&a, 0, sizeof(a));
+    a.n = n_entries;
+    a.cols = (int32_t)cols;
+    a.sf_cols = (int32_t)(cols / block_of(fmt));
+    a.sf_stride = layout == MXQ_SF_SWIZZLED ? (int32_t)round_up(a.sf_cols, 4) : a.sf_cols;
+    int64_t units = 0;
+    for (int i = 0; i < n_entries; ++i) {
+        const mxq_entry &e = entries[i];
+        if (e.rows < 0 || e.rows >= (int64_t)1 << 31) return MXQ_EINVAL;
+        if (e.rows > 0) {
+            if (!e.src || !e.payload || !e.scales) return MXQ_EINVAL;
+            if (fmt == MXQ_NVFP4 && !e.global_scale) return MXQ_EINVAL;
+            if (e.src_ld < cols || e.src_ld % 8 != 0 || e.src_ld >= (int64_t)1 << 31)
+                return MXQ_ESHAPE;
+            if (!aligned16(e.src) || !aligned16(e.payload)) return MXQ_ESHAPE;
+            if (layout == MXQ_SF_SWIZZLED && !aligned16(e.scales)) return MXQ_ESHAPE;
+        }
+        a.e[i].src = static_cast<const uint16_t *>(e.src);
+        a.e[i].payload = static_cast<uint8_t *>(e.payload);
+        a.e[i].scales = static_cast<uint8_t *>(e.scales);
+        a.e[i].g = e.global_scale;
+        a.e[i].ld = e.src_ld;
+        a.e[i].rows = (int32_t)e.rows;
+        a.e[i].unit_begin = (int32_t)units;
+        units += units_for(e.rows, layout);
+        if (units >= (int64_t)1 << 31) return MXQ_ESHAPE;
+    }
+    a.total_units = (int32_t)units;
+    if (units == 0) return MXQ_OK;
+    hipError_t err = launch_grouped(fmt, layout, a, grid_for(units), (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;
+}
+
+int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols, const int64_t *split_rows,
+                      int n_splits, const float *global_scale, void *payload, void *scales,
+                      float *row_amax, int layout, void *stream) {
+    if (!valid_layout(layout) || !split_rows || n_splits < 1 || total_rows < 0 ||
+        total_rows >= (int64_t)1 << 31)
+        return MXQ_EINVAL;
+    int64_t sum = 0;
+    for (int i = 0; i < n_splits; ++i) {
+        if (split_rows[i] < 0) return MXQ_EINVAL;
+        sum += split_rows[i];
+    }
+    if (sum != total_rows) return MXQ_EINVAL;
+    if (cols <= 0 || cols % 16 != 0 || cols > kMaxColsNv) return MXQ_ESHAPE;
+    if (total_rows == 0) return MXQ_OK;
+    if (!src || !global_scale || !payload || !scales) return MXQ_EINVAL;
+    if (!aligned16(src) || !aligned16(payload)) return MXQ_ESHAPE;
+    if (layout == MXQ_SF_SWIZZLED && !aligned16(scales)) return MXQ_ESHAPE;
+
+    const int64_t C = cols / 16;
+    const int64_t Cs = layout == MXQ_SF_SWIZZLED ? round_up(C, 4) : C;
+    int64_t row_base = 0, scale_base = 0;
+    for (int first = 0; first < n_splits; first += kMaxSplitsPerLaunch) {
+        const int n = n_splits - first < kMaxSplitsPerLaunch ? n_splits - first
+                                                             : kMaxSplitsPerLaunch;
+        SplitArgs a;
+        memset(&a, 0, sizeof(a));
+        a.src = static_cast<const uint16_t *>(src) + row_base * cols;
+        a.payload = static_cast<uint8_t *>(payload) + row_base * (cols / 2);
+        a.scales = static_cast<uint8_t *>(scales) + scale_base;
+        a.row_amax = row_amax ? row_amax + row_base : nullptr;
+        a.g = global_scale;
+        a.cols = (int32_t)cols;
+        a.sf_cols = (int32_t)C;
+        a.sf_stride = (int32_t)Cs;
+        a.n = n;
+        int64_t rows = 0, units = 0, sbytes = 0;
+        for (int j = 0; j < n; ++j) {
+            const int64_t m = split_rows[first + j];
+            a.row_off[j] = (int32_t)rows;
+            a.unit_off[j] = (int32_t)units;
+            rows += m;
+            units += units_for(m, layout);
+            sbytes += sf_bytes(m, C, layout);
+        }
+        a.row_off[n] = (int32_t)rows;
+        a.unit_off[n] = (int32_t)units;
+        a.total_units = (int32_t)units;
+        if (units > 0) {
+            hipError_t err = launch_split(layout, a, grid_for(units), (hipStream_t)stream);
+            if (err != hipSuccess) return MXQ_ELAUNCH;
+        }
+        row_base += rows;
+        scale_base += sbytes;
+    }
+    return MXQ_OK;
+}
+
+int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual,
+                        const void *gamma, float eps, int64_t T, int64_t H,
+                        const float *global_scale, void *residual_out, void *norm_out,
+                        void *payload, void *scales, void *stream) {
+    if (!valid_fmt(fmt) || !valid_layout(layout)) return MXQ_EINVAL;
+    if (!(eps > 0.0f) || !(eps < 3.4e38f) || T < 0 || T >= (int64_t)1 << 31) return MXQ_EINVAL;
+    if (H <= 0 || H % block_of(fmt) != 0 || H > kMaxFusedH) return MXQ_ESHAPE;
+    const int64_t C = H / block_of(fmt);
+    // The swizzled tile needs four scale columns; a hidden size that would pad
+    // scale columns is refused rather than leaving unreachable padding.
+    if (layout == MXQ_SF_SWIZZLED && C % 4 != 0) return MXQ_ESHAPE;
+    if (T == 0) return MXQ_OK;
+    if (!x || !residual || !gamma || !residual_out || !norm_out || !payload || !scales)
+        return MXQ_EINVAL;
+    if (fmt == MXQ_NVFP4 && !global_scale) return MXQ_EINVAL;
+    if (!aligned16(x) || !aligned16(residual) || !aligned16(gamma) || !aligned16(residual_out) ||
+        !aligned16(norm_out) || !aligned16(payload) || !aligned16(scales))
+        return MXQ_ESHAPE;
+    FusedArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = static_cast<const uint16_t *>(x);
+    a.res = static_cast<const uint16_t *>(residual);
+    a.gamma = static_cast<const uint16_t *>(gamma);
+    a.res_out = static_cast<uint16_t *>(residual_out);
+    a.norm_out = static_cast<uint16_t *>(norm_out);
+    a.payload = static_cast<uint8_t *>(payload);
+    a.scales = static_cast<uint8_t *>(scales);
+    a.g = global_scale;
+    a.eps = eps;
+    a.T = (int32_t)T;
+    a.H = (int32_t)H;
+    a.sf_cols = (int32_t)C;
+    a.sf_stride = (int32_t)(layout == MXQ_SF_SWIZZLED ? round_up(C, 4) : C);
+    const int64_t units = units_for(T, layout);
+    a.total_units = (int32_t)units;
+    hipError_t err = launch_fused(fmt, layout, a, grid_for(units), (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;
+}
+
+int scale_swizzle(const void *linear, int64_t rows, int64_t sf_cols, void *swizzled, void *stream) {
+    if (rows < 0 || sf_cols <= 0 || rows >= (int64_t)1 << 40 || sf_cols >= (int64_t)1 << 31)
+        return MXQ_EINVAL;
+    if (rows == 0) return MXQ_OK;
+    if (!linear || !swizzled) return MXQ_EINVAL;
+    if (!aligned16(swizzled)) return MXQ_ESHAPE;
+    SwizzleArgs a;
+    a.lin = static_cast<const uint8_t *>(linear);
+    a.swz = static_cast<uint8_t *>(swizzled);
+    a.rows = rows;
+    a.cols = sf_cols;
+    a.tiles_per_band = round_up(sf_cols, 4) / 4;
+    a.n_vec = round_up(rows, 128) * round_up(sf_cols, 4) / 16;
+    int64_t grid = (a.n_vec + kThreads - 1) / kThreads;
+    if (grid > 65536) grid = 65536;
+    hipError_t err = launch_swizzle(a, grid_for(grid), (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;
+}
+
+}  // extern "C"

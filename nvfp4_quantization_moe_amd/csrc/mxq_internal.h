@@ -1,0 +1,95 @@
+// mxq_internal.h -- kernel argument tables and launchers shared by the C ABI
+// (mxq_api.hip) and the kernels (mxq_kernels.hip).  Not part of the public
+// interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxq.h"
+
+namespace mxq {
+
+constexpr int kThreads = 256;  // 4 waves per workgroup
+constexpr int kUnitRows = 32;  // rows per work unit (8 per wave)
+constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
+
+// One grouped-launch descriptor.  The whole table travels in the kernel
+// arguments, so a grouped call is one dispatch with no device-side table.
+struct GEntry {
+    const uint16_t *src;  // bf16 bits
+    uint8_t *payload;
+    uint8_t *scales;
+    const float *g;       // NVFP4 encode scale (device scalar)
+    int64_t ld;           // row stride, elements
+    int32_t rows;
+    int32_t unit_begin;   // index of this entry's first work unit
+};
+
+struct GroupArgs {
+    GEntry e[MXQ_MAX_GROUP];
+    int32_t n;            // entries
+    int32_t cols;
+    int32_t sf_cols;      // C = cols / block
+    int32_t sf_stride;    // swizzled: round_up(C, 4); linear: C
+    int32_t total_units;
+};
+
+constexpr int kMaxSplitsPerLaunch = 256;
+
+// Up to 256 consecutive splits of a concatenated activation.  Work units are
+// 32-row groups that never straddle two experts.
+struct SplitArgs {
+    const uint16_t *src;  // global row 0 of this launch's first split
+    uint8_t *payload;     // same row
+    uint8_t *scales;      // this launch's first split's scale region
+    float *row_amax;      // same row (may be null)
+    const float *g;
+    int32_t cols;
+    int32_t sf_cols;
+    int32_t sf_stride;
+    int32_t n;            // splits in this launch
+    int32_t total_units;
+    int32_t row_off[kMaxSplitsPerLaunch + 1];   // prefix sums of split rows
+    int32_t unit_off[kMaxSplitsPerLaunch + 1];  // prefix sums of split units
+};
+
+struct FusedArgs {
+    const uint16_t *x;
+    const uint16_t *res;
+    const uint16_t *gamma;
+    uint16_t *res_out;
+    uint16_t *norm_out;
+    uint8_t *payload;
+    uint8_t *scales;
+    const float *g;
+    float eps;
+    int32_t T;
+    int32_t H;
+    int32_t sf_cols;
+    int32_t sf_stride;
+    int32_t total_units;
+};
+
+struct SwizzleArgs {
+    const uint8_t *lin;
+    uint8_t *swz;
+    int64_t rows;
+    int64_t cols;        // scale columns C
+    int64_t tiles_per_band;  // round_up(C, 4) / 4
+    int64_t n_vec;       // 16-byte output vectors
+};
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_grouped(int fmt, int layout, const GroupArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_split(int layout, const SplitArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_swizzle(const SwizzleArgs &a, int64_t grid, hipStream_t s);
+
+// Largest supported row length (keeps one unit's staged scales within 32 KiB
+// of LDS and a fused row within registers).
+constexpr int64_t kMaxColsMx = 32768;
+constexpr int64_t kMaxColsNv = 16384;
+constexpr int64_t kMaxFusedH = 16384;
+
+}  // namespace mxq

@@ -1,0 +1,175 @@
+"""GPU parity of nvfp4_quant_split, rmsnorm_quant_fused and scale_swizzle.
+
+Split: the routed-activation workload at full size ([8192,7168], 256
+experts, 10 empty) and a hand split set with uneven, empty and
+128-multiple splits; canary-filled bulk buffers; requantizing one expert
+leaves every other byte untouched.  Fused: T in {1,16,64,256,1024,4096} at
+H = 7168: residual_out exact, norm_out within 1 bf16 ulp of the oracle,
+payload and scales equal to the oracle's quantization of the GPU norm_out,
+padded scale rows zero.  Swizzle: equals the oracle and the quantizer's own
+swizzled output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_quantization_moe_amd as mxq
+from nvfp4_quantization_moe_amd import workloads
+from helpers import bf16_bits
+from gpu_common import CANARY, canary_buffer, g_of, guard_intact, say, u8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_split(x, split, g, layout):
+    T, H = x.shape
+    total = mxq.split_scale_offset(split, len(split), H, mxq.NVFP4, layout)
+    p, pw = canary_buffer(T * H // 2)
+    s, sw = canary_buffer(total)
+    a = torch.full((T + 1024,), float("nan"), dtype=torch.float32, device=DEV)
+    mxq.nvfp4_quant_split(x, split, g, layout, p.view(T, H // 2), s, a[:T])
+    torch.cuda.synchronize()
+    assert guard_intact(pw, T * H // 2) and guard_intact(sw, total)
+    assert torch.all(torch.isnan(a[T:])).item()
+    return p, s, a[:T], total
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_split_hand_set(orc, layout):
+    split = [0, 1, 127, 128, 129, 0, 255, 256, 3, 31, 32, 33, 0]
+    T, H = sum(split), 7168
+    gen = torch.Generator().manual_seed(77)
+    x_cpu = (torch.randn(T, H, generator=gen) * 2).to(torch.bfloat16)
+    x = x_cpu.to(DEV)
+    g = g_of(x)
+    say("split hand set, layout", layout)
+    p, s, a, total = run_split(x, split, g, layout)
+    op, os_, oa = orc.nvfp4_split(bf16_bits(x_cpu), split, float(g), layout)
+    assert np.array_equal(u8(p), op.ravel())
+    assert np.array_equal(u8(s), os_)
+    assert np.array_equal(a.cpu().numpy(), oa)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_split_routed_activation_full_size(orc, layout):
+    x_cpu, split = workloads.routed_activation()
+    assert sum(split) == 8192 and sum(1 for m in split if m == 0) >= 10
+    x = x_cpu.to(DEV)
+    g = g_of(x)
+    say("split [8192,7168] x 256 experts, layout", layout)
+    p, s, a, total = run_split(x, split, g, layout)
+    op, os_, oa = orc.nvfp4_split(bf16_bits(x_cpu), split, float(g), layout)
+    assert np.array_equal(u8(p), op.ravel())
+    assert np.array_equal(u8(s), os_)
+    assert np.array_equal(a.cpu().numpy(), oa)
+    # requantizing one expert into its own slice changes nothing else
+    i = max(range(len(split)), key=lambda k: split[k])
+    o = sum(split[:i])
+    m = split[i]
+    base = mxq.split_scale_offset(split, i, 7168, mxq.NVFP4, layout)
+    size = mxq.split_scale_offset(split, i + 1, 7168, mxq.NVFP4, layout) - base
+    before_p, before_s = u8(p).copy(), u8(s).copy()
+    p[o * 3584:(o + m) * 3584].fill_(CANARY)
+    s[base:base + size].fill_(CANARY)
+    say("requantize expert", i, "rows", m)
+    mxq.nvfp4_quant_split(x[o:o + m], [m], g, layout, p[o * 3584:(o + m) * 3584].view(m, 3584),
+                          s[base:base + size], a[o:o + m])
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(p), before_p) and np.array_equal(u8(s), before_s)
+
+
+def test_split_equals_grouped_per_expert(orc):
+    """The split's per-expert storage equals quantizing each slice alone."""
+    split = [5, 0, 130, 64, 1]
+    T, H = sum(split), 1024
+    x = (torch.randn(T, H) * 3).to(torch.bfloat16).to(DEV)
+    g = g_of(x)
+    say("split vs grouped")
+    p, s, a, total = run_split(x, split, g, mxq.SWIZZLED)
+    o = 0
+    for i, m in enumerate(split):
+        base = mxq.split_scale_offset(split, i, H)
+        if m:
+            gp, gs = mxq.mx_quant_grouped(mxq.NVFP4, mxq.SWIZZLED, [x[o:o + m]],
+                                          global_scales=g)
+            assert np.array_equal(u8(gp[0]), u8(p)[o * H // 2:(o + m) * H // 2])
+            assert np.array_equal(u8(gs[0]), u8(s)[base:base + gs[0].numel()])
+        o += m
+
+
+def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in bf16 ulps between bit patterns (sign-magnitude ordered)."""
+    def key(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
+@pytest.mark.parametrize("T", [1, 16, 64, 256, 1024, 4096])
+def test_fused_epilogue(orc, T):
+    H = 7168
+    x_c, r_c, g_c = workloads.epilogue_inputs(T, H)
+    x, r, gm = x_c.to(DEV), r_c.to(DEV), g_c.to(DEV)
+    nb = mxq.scale_bytes(T, H, mxq.MXFP8, mxq.SWIZZLED)
+    ro = torch.empty_like(x)
+    no = torch.empty_like(x)
+    pay, pw = canary_buffer(T * H)
+    sc, sw = canary_buffer(nb)
+    say("fused T =", T)
+    mxq.rmsnorm_quant_fused(x, r, gm, 1e-6, mxq.MXFP8, mxq.SWIZZLED,
+                            out=(ro, no, pay.view(T, H), sc))
+    torch.cuda.synchronize()
+    assert guard_intact(pw, T * H) and guard_intact(sw, nb)
+    oro, ono = orc.add_rmsnorm(bf16_bits(x_c), bf16_bits(r_c), bf16_bits(g_c), 1e-6)
+    assert np.array_equal(bf16_bits(ro), oro)
+    d = bf16_ulp_diff(bf16_bits(no), ono)
+    assert d.max() <= 1, d.max()
+    # the quantized form is the quantization of the GPU's own norm_out
+    qp, qs = orc.quantize(orc.MXFP8, orc.SWIZZLED, bf16_bits(no))
+    assert np.array_equal(u8(pay), qp.ravel())
+    assert np.array_equal(u8(sc), qs)
+    # invented scale rows T..round_up(T,128) are zero
+    C = H // 32
+    rows_pad = -(-T // 128) * 128
+    offs = [orc.sf_offset(rr, c, C, orc.SWIZZLED) for rr in range(T, rows_pad) for c in (0, C - 1)]
+    assert np.all(u8(sc)[offs] == 0)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_fused_formats_layouts(orc, fmt, layout):
+    T, H = 77, 1024
+    x_c, r_c, g_c = workloads.epilogue_inputs(T, H, seed=31)
+    x, r, gm = x_c.to(DEV), r_c.to(DEV), g_c.to(DEV)
+    gs = torch.tensor([37.5], dtype=torch.float32, device=DEV)
+    say("fused fmt/layout", fmt, layout)
+    ro, no, pay, sc = mxq.rmsnorm_quant_fused(x, r, gm, 1e-5, fmt, layout, gs if fmt else None)
+    torch.cuda.synchronize()
+    oro, ono = orc.add_rmsnorm(bf16_bits(x_c), bf16_bits(r_c), bf16_bits(g_c), 1e-5)
+    assert np.array_equal(bf16_bits(ro), oro)
+    assert bf16_ulp_diff(bf16_bits(no), ono).max() <= 1
+    qp, qs = orc.quantize(fmt, layout, bf16_bits(no), g=37.5)
+    assert np.array_equal(u8(pay), qp.ravel()) and np.array_equal(u8(sc), qs)
+
+
+@pytest.mark.parametrize("R,C", [(1, 1), (130, 8), (255, 7), (300, 17), (4096, 224), (3, 448)])
+def test_scale_swizzle(orc, R, C):
+    lin = torch.randint(1, 256, (R, C), dtype=torch.uint8)
+    say("swizzle", R, C)
+    n = (-(-R // 128) * 128) * (-(-C // 4) * 4)
+    out, whole = canary_buffer(n)
+    mxq.scale_swizzle(lin.to(DEV), out)
+    torch.cuda.synchronize()
+    assert guard_intact(whole, n)
+    assert np.array_equal(u8(out), orc.scale_swizzle(lin.numpy()))
+
+
+def test_swizzle_of_linear_equals_swizzled_quant(orc):
+    x = (torch.randn(300, 4096) * 0.02).to(torch.bfloat16).to(DEV)
+    say("layouts agree")
+    _, s_lin = mxq.mx_quant_grouped(mxq.MXFP8, mxq.LINEAR, [x])
+    _, s_swz = mxq.mx_quant_grouped(mxq.MXFP8, mxq.SWIZZLED, [x])
+    conv = mxq.scale_swizzle(s_lin[0].view(300, 128))
+    torch.cuda.synchronize()
+    assert torch.equal(conv, s_swz[0])
