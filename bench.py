@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--cpu-experts", type=int, default=16,
                     help="gate_up experts in the CPU oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy first (hardware-counter calibration)")
     return ap.parse_args()
 
 
@@ -97,6 +99,13 @@ def main():
             if events is not None:
                 events[k][1].record()
 
+    if args.calib_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"[bench] warmup {args.warmup} steps ({len(calls)} launches/step)")
     for _ in range(args.warmup):
         step()

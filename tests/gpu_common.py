@@ -33,6 +33,8 @@ def guard_intact(whole: torch.Tensor, n: int) -> bool:
 
 def g_of(x: torch.Tensor) -> torch.Tensor:
     """fp32 encode scale 2688 / amax(x) (1 for an all-zero tensor), on x's device."""
+    if x.numel() == 0:
+        return torch.ones(1, dtype=torch.float32, device=x.device)
     a = x.float().abs().amax()
     return torch.where(a > 0, 2688.0 / a, torch.ones_like(a)).reshape(1)
 
