@@ -19,12 +19,11 @@ inline bool valid_layout(int l) { return l == MXQ_SF_LINEAR || l == MXQ_SF_SWIZZ
 inline int64_t block_of(int fmt) { return fmt == MXQ_MXFP8 ? 32 : 16; }
 inline int64_t max_cols(int fmt) { return fmt == MXQ_MXFP8 ? kMaxColsMx : kMaxColsNv; }
 
-// Work units (32-row groups) for a tensor of `rows` rows.  Swizzled units
+// Row groups of `per` rows for a tensor of `rows` rows.  Swizzled groups
 // cover the padded rows too, so the padding is written by the kernel.
-inline int64_t units_for(int64_t rows, int layout) {
+inline int64_t row_groups(int64_t rows, int layout, int per) {
     if (rows <= 0) return 0;
-    return layout == MXQ_SF_SWIZZLED ? round_up(rows, 128) / kUnitRows
-                                     : (rows + kUnitRows - 1) / kUnitRows;
+    return layout == MXQ_SF_SWIZZLED ? round_up(rows, 128) / per : (rows + per - 1) / per;
 }
 
 inline int64_t grid_for(int64_t units) {
@@ -85,6 +84,7 @@ int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries
     a.cols = (int32_t)cols;
     a.sf_cols = (int32_t)(cols / block_of(fmt));
     a.sf_stride = layout == MXQ_SF_SWIZZLED ? (int32_t)round_up(a.sf_cols, 4) : a.sf_cols;
+    a.n_cc = (int32_t)((cols + kChunk - 1) / kChunk);
     int64_t units = 0;
     for (int i = 0; i < n_entries; ++i) {
         const mxq_entry &e = entries[i];
@@ -104,7 +104,7 @@ int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries
         a.e[i].ld = e.src_ld;
         a.e[i].rows = (int32_t)e.rows;
         a.e[i].unit_begin = (int32_t)units;
-        units += units_for(e.rows, layout);
+        units += row_groups(e.rows, layout, kUnitRows) * a.n_cc;
         if (units >= (int64_t)1 << 31) return MXQ_ESHAPE;
     }
     a.total_units = (int32_t)units;
@@ -154,7 +154,7 @@ int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols, const i
             a.row_off[j] = (int32_t)rows;
             a.unit_off[j] = (int32_t)units;
             rows += m;
-            units += units_for(m, layout);
+            units += row_groups(m, layout, kRowUnit);
             sbytes += sf_bytes(m, C, layout);
         }
         a.row_off[n] = (int32_t)rows;
@@ -203,7 +203,7 @@ int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual
     a.H = (int32_t)H;
     a.sf_cols = (int32_t)C;
     a.sf_stride = (int32_t)(layout == MXQ_SF_SWIZZLED ? round_up(C, 4) : C);
-    const int64_t units = units_for(T, layout);
+    const int64_t units = row_groups(T, layout, kRowUnit);
     a.total_units = (int32_t)units;
     hipError_t err = launch_fused(fmt, layout, a, grid_for(units), (hipStream_t)stream);
     return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;

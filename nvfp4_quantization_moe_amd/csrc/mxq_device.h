@@ -2,11 +2,13 @@
 // bf16 unpacking, block-amax reductions across lanes with DPP, and the
 // MXFP8 / NVFP4 scale and element encoders.
 //
-// The encoders implement, in fp32/integer arithmetic, the exact rules of the
-// formats (OCP OFP8 E4M3 with largest finite 448; OCP MX E8M0 and E2M1; the
-// NVFP4 16-element block with an E4M3 scale under an fp32 encode scale):
-// round to nearest even, sign of zero kept, saturation where a value can
-// exceed the format.  See include/mxq.h for the block rules.
+// The encoders implement the exact rules of the formats (OCP OFP8 E4M3 with
+// largest finite 448; OCP MX E8M0 and E2M1; the NVFP4 16-element block with an
+// E4M3 scale under an fp32 encode scale): round to nearest even, sign of zero
+// kept, saturation where a value can exceed the format.  Element rounding uses
+// gfx950's scaled conversion instructions in the forms shown (by exhaustive
+// comparison with the rules) to reproduce them bit for bit.  See
+// include/mxq.h for the block rules.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -76,39 +78,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---- E4M3 --------------------------------------------------------------------
-// Encode fp32 y with |y| <= 448 (or any y when kSaturate): round to nearest
-// even on the E4M3 grid, subnormals below 2^-6 on a 2^-9 grid, sign kept.
-template <bool kSaturate>
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-    uint32_t u = __float_as_uint(y);
-    uint32_t s = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    if (kSaturate) a = min(a, 0x43E00000u);  // 448; also catches +inf
-    // normal range: keep 3 mantissa bits, RNE at bit 20, rebias 127 -> 7
-    uint32_t rn = a + 0x7FFFFu + ((a >> 20) & 1u);
-    uint32_t cn = (rn >> 20) - (120u << 3);
-    // below 2^-6: adding 2^14 (ulp 2^-9) rounds |y| to the subnormal grid
-    uint32_t cs = __float_as_uint(__uint_as_float(a) + 16384.0f) - 0x46800000u;
-    return (a < 0x3C800000u ? cs : cn) | s;
-}
-
 // Decode a non-negative, non-NaN E4M3 code.
 __device__ __forceinline__ float e4m3_decode_pos(uint32_t k) {
     uint32_t e = k >> 3, m = k & 7u;
     return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
-
-// ---- E2M1 --------------------------------------------------------------------
-// Encode fp32 y: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code,
-// saturating at 6, sign in bit 3.
-__device__ __forceinline__ uint32_t e2m1_encode(float y) {
-    uint32_t u = __float_as_uint(y);
-    uint32_t s = (u >> 28) & 0x8u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t rn = a + 0x1FFFFFu + ((a >> 22) & 1u);         // keep 1 mantissa bit
-    uint32_t cn = min((rn >> 22) - ((127u - 1u) << 1), 7u);  // rebias 127 -> 1
-    uint32_t cs = __float_as_uint(__uint_as_float(a) + 4194304.0f) - 0x4A800000u;  // 0.5 grid
-    return (a < 0x3F800000u ? cs : cn) | s;
 }
 
 // ---- MXFP8 block rule --------------------------------------------------------
@@ -121,26 +94,32 @@ __device__ __forceinline__ uint32_t mx_scale_code(uint32_t amax_bits) {
     return E == 0 ? 0u : (uint32_t)max(c, 0);
 }
 
-// Element multiplier 2^(127-c); code 0 (scale 2^-127, not a normal fp32)
-// flushes the reciprocal to zero.  Codes above 253 cannot occur for bf16.
-__device__ __forceinline__ float mx_multiplier(uint32_t c) {
-    return c == 0 ? 0.0f : __uint_as_float((254u - c) << 23);
-}
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-// Quantize 8 bf16 values (one lane's share of a 32-element block) with the
-// multiplier m; returns 8 E4M3 bytes.  x*m is exact (power of two) except
-// below 2^-126, where the code is a signed zero either way.
-__device__ __forceinline__ u32x2 mx_encode8(u32x4 v, float m) {
-    u32x2 out;
-    uint32_t b[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        b[2 * j] = e4m3_encode<false>(bf16_lo(v[j]) * m);
-        b[2 * j + 1] = e4m3_encode<false>(bf16_hi(v[j]) * m);
-    }
-    out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-    out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-    return out;
+// Quantize 8 bf16 values (one lane's share of a 32-element block) under
+// scale code c; returns 8 E4M3 bytes, element k in byte k.
+//
+// gfx950's v_cvt_scalef32_pk_fp8_bf16 takes the scale as an fp32 whose
+// exponent field e divides the input by 2^(e-127) before rounding to E4M3
+// (nearest even, sign kept), so e = c gives x * 2^(127-c) exactly.  Its result
+// equals the E4M3 rule for every bf16 input and every code with
+// |x| * 2^(127-c) <= 448, i.e. every input a block with code c can hold (the
+// GPU parity tests enumerate all of them).  Code 0 stands for a scale of
+// 2^-127, whose reciprocal is flushed to zero: there every element must
+// encode as a signed zero, which e = 254 (divide by 2^127) yields because
+// such blocks hold only magnitudes <= 448 * 2^-127.
+__device__ __forceinline__ u32x2 mx_encode8(u32x4 v, uint32_t c) {
+    const float sc = __uint_as_float((c == 0 ? 254u : c) << 23);
+    // The pairs are built from one whole-vector cast: this compiler folds a
+    // bit_cast of each ext-vector element (v.y, v.z, ...) to element 0.
+    const v8bf e = __builtin_bit_cast(v8bf, v);
+    v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v2s{0, 0}, v2bf{e[0], e[1]}, sc, false);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, v2bf{e[2], e[3]}, sc, true);
+    v2s hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v2s{0, 0}, v2bf{e[4], e[5]}, sc, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, v2bf{e[6], e[7]}, sc, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 // ---- NVFP4 block rule --------------------------------------------------------
@@ -149,32 +128,44 @@ struct Nv4Scale {
     float mult;     // element multiplier fp32(g / s_q), 0 when flushed
 };
 
-// s = fp32(fp32(amax / 6) * g); code = E4M3(s) saturating; multiplier
-// fp32(g / decode(code)), zero when the decoded scale is zero or the
-// multiplier is not a normal fp32 number.  Divisions are IEEE (the build
-// keeps fp32 division correctly rounded and denormals enabled).
+// fp32(a / 6), correctly rounded, for a non-negative bf16 value a: one
+// product with fp32(1/6) and one fused correction step.  Checked exactly
+// against the rounded quotient for every finite non-negative bf16 value.
+__device__ __forceinline__ float div6(float a) {
+    const float r6 = 0.16666667163372040f;  // fp32(1/6)
+    const float q = a * r6;
+    const float r = __builtin_fmaf(-q, 6.0f, a);
+    return __builtin_fmaf(r, r6, q);
+}
+
+// s = fp32(fp32(amax / 6) * g); code = E4M3(s), saturating at 448; multiplier
+// fp32(g / decode(code)) (IEEE division), zero when the decoded scale is zero
+// or the multiplier is not a normal fp32 number.
 __device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g) {
-    float a = __uint_as_float(amax_bits << 16);
-    float t = a / 6.0f;
-    float s = t * g;
+    const float s = div6(__uint_as_float(amax_bits << 16)) * g;
     Nv4Scale r;
-    r.code = e4m3_encode<true>(s);
-    float sq = e4m3_decode_pos(r.code);
-    float m = g / sq;
+    // v_cvt_scalef32_pk_fp8_f32 (scale 1.0) rounds to nearest even and keeps
+    // values up to 448 exact to the rule; larger values are clamped first.
+    const v2s k = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, __builtin_fminf(s, 448.0f),
+                                                           0.0f, 1.0f, false);
+    r.code = __builtin_bit_cast(uint32_t, k) & 0xFFu;
+    const float sq = e4m3_decode_pos(r.code);
+    const float m = g / sq;
     r.mult = (sq == 0.0f || !(m >= 0x1p-126f)) ? 0.0f : m;
     return r;
 }
 
 // Quantize 8 bf16 values with multiplier m; returns 4 bytes of packed E2M1
-// (element 2j in the low nibble of byte j).
+// (element 2j in the low nibble of byte j).  fp32(x * m) is formed first;
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 then rounds each fp32 to E2M1
+// exactly as the rule does (nearest, ties to the even code, saturation at 6,
+// sign kept), first operand in the low nibble.
 __device__ __forceinline__ uint32_t nv_encode8(u32x4 v, float m) {
     uint32_t out = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t lo = e2m1_encode(bf16_lo(v[j]) * m);
-        uint32_t hi = e2m1_encode(bf16_hi(v[j]) * m);
-        out |= (lo | (hi << 4)) << (8 * j);
-    }
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, bf16_lo(v.x) * m, bf16_hi(v.x) * m, 1.0f, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, bf16_lo(v.y) * m, bf16_hi(v.y) * m, 1.0f, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, bf16_lo(v.z) * m, bf16_hi(v.z) * m, 1.0f, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, bf16_lo(v.w) * m, bf16_hi(v.w) * m, 1.0f, 3);
     return out;
 }
 

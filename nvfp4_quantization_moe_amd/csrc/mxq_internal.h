@@ -11,8 +11,9 @@
 namespace mxq {
 
 constexpr int kThreads = 256;  // 4 waves per workgroup
-constexpr int kUnitRows = 32;  // rows per work unit (8 per wave)
+constexpr int kUnitRows = 32;  // rows per grouped work unit (8 per wave)
 constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
+constexpr int kRowUnit = 4;    // rows per split/fused work unit (1 per wave)
 
 // One grouped-launch descriptor.  The whole table travels in the kernel
 // arguments, so a grouped call is one dispatch with no device-side table.
@@ -32,13 +33,14 @@ struct GroupArgs {
     int32_t cols;
     int32_t sf_cols;      // C = cols / block
     int32_t sf_stride;    // swizzled: round_up(C, 4); linear: C
+    int32_t n_cc;         // 512-column chunks per row
     int32_t total_units;
 };
 
 constexpr int kMaxSplitsPerLaunch = 256;
 
 // Up to 256 consecutive splits of a concatenated activation.  Work units are
-// 32-row groups that never straddle two experts.
+// 4-row groups that never straddle two experts.
 struct SplitArgs {
     const uint16_t *src;  // global row 0 of this launch's first split
     uint8_t *payload;     // same row

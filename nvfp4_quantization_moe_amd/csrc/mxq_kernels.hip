@@ -1,18 +1,31 @@
 // mxq_kernels.hip -- gfx950 kernels for grouped / split block quantization,
 // the fused residual + RMSNorm + quantize epilogue, and the scale swizzle.
 //
-// Work decomposition (all quantize kernels): a workgroup of 4 waves takes a
-// 32-row work unit; each wave owns 8 rows and streams them in 512-element
-// steps, each lane loading 16 contiguous bytes (8 bf16), so a wave load is
-// 1 KiB of one row.  A block of 32 (MXFP8) or 16 (NVFP4) elements spans 4 or
-// 2 adjacent lanes; its amax is reduced with DPP quad permutes, never through
-// LDS.  Payload bytes go straight to HBM (8 or 4 contiguous bytes per lane);
-// scale bytes are staged in LDS and written out once per unit.  With the
-// swizzled layout a unit takes rows band*128 + 32*wave + 8*g + i of one
-// 128-row band, which fill exactly one full 128-byte line of every 512-byte
-// tile, so the staged scales leave as whole lines, padding included.  No
-// atomics, no scratch buffers, no inter-workgroup ordering: every byte has
-// exactly one writer, and the result does not depend on the grid size.
+// All of this is streaming work bounded by HBM bandwidth, so the kernels are
+// shaped like a well-behaved copy: many small workgroups, every load of a
+// workgroup issued before any of its stores, 16 contiguous bytes per lane
+// (a wave load is 1 KiB of one row), and each lane's output bytes contiguous.
+//
+// Grouped (k_grouped): a work unit is 32 rows x 512 columns of one expert,
+// 8 rows per wave.  A block of 32 (MXFP8) or 16 (NVFP4) elements spans 4 or 2
+// adjacent lanes; its amax is reduced with DPP quad permutes, never through
+// LDS.  Payload bytes go straight to HBM; scale bytes are staged in LDS.  With
+// the swizzled layout the unit's rows are band*128 + 32*wave + 8*g + i
+// (i = 0..7) of one 128-row band, which fill exactly one 128-byte line of each
+// 512-byte tile the chunk touches, so scales leave as whole lines, padding
+// included.
+//
+// Split and fused (k_split, k_fused): they need whole rows (row amax, the
+// RMSNorm sum of squares), so one wave owns one row and holds all of it in
+// registers; a unit is 4 rows.  Swizzled units take rows band*128 + 32*wave +
+// gi (gi = 0..31), so a unit writes one 16-byte piece of each tile line and
+// the 8 consecutive units that complete a line run on the same XCD.
+//
+// Units are assigned to workgroups XCD by XCD: hardware dispatches workgroup b
+// to XCD b mod 8, and unit order is remapped so that each XCD (with its own
+// L2) walks a contiguous range of units.  No atomics, no scratch, no
+// inter-workgroup ordering: every byte has one writer, and the bytes do not
+// depend on the grid size.
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
@@ -31,20 +44,21 @@ struct FmtTraits<MXQ_NVFP4> {
     static constexpr int kLanesPerBlock = 2;
 };
 
-// Quantize one lane's 8 elements; the lanes of a block cooperate through DPP.
-// Returns the block's scale byte (every lane of the block holds it) and the
-// lane's payload: 8 bytes (MXFP8) or 4 bytes in pay.x (NVFP4).
+// Quantize one lane's 8 elements; the lanes of a block cooperate through DPP
+// (all lanes of a block must be active).  Returns the block's scale byte
+// (every lane of the block holds it) and the lane's payload: 8 bytes (MXFP8)
+// or 4 bytes in pay.x (NVFP4).
 template <int FMT>
 __device__ __forceinline__ uint32_t quant8(u32x4 v, float g, u32x2 &pay) {
     uint32_t a = amax_bits8(v);
     if constexpr (FMT == MXQ_MXFP8) {
         a = block_max4(a);
-        uint32_t c = mx_scale_code(a);
-        pay = mx_encode8(v, mx_multiplier(c));
+        const uint32_t c = mx_scale_code(a);
+        pay = mx_encode8(v, c);
         return c;
     } else {
         a = block_max2(a);
-        Nv4Scale s = nv_scale(a, g);
+        const Nv4Scale s = nv_scale(a, g);
         pay.x = nv_encode8(v, s.mult);
         pay.y = 0;
         return s.code;
@@ -59,143 +73,166 @@ __device__ __forceinline__ void store_payload(uint8_t *row_payload, int col, u32
         *reinterpret_cast<uint32_t *>(row_payload + (col >> 1)) = pay.x;
 }
 
-// Row of the unit handled by wave q at slot i.
-template <int LAYOUT>
-__device__ __forceinline__ int unit_row(int lu, int q, int i) {
-    if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-        return (lu >> 2) * 128 + 32 * q + 8 * (lu & 3) + i;
-    else
-        return lu * kUnitRows + 8 * q + i;
+// Workgroup b -> unit, contiguous per XCD (bijective on [0, n)).
+__device__ __forceinline__ int xcd_unit(int b, int n) {
+    const int q = n >> 3, r = n & 7, x = b & 7;
+    return x * q + min(x, r) + (b >> 3);
 }
 
-template <int LAYOUT>
-__device__ __forceinline__ int stage_index(int q, int i, int c, int sf_stride) {
-    if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-        return stage_index_swz(q, i, c);
-    else
-        return (8 * q + i) * sf_stride + c;
-}
-
-__device__ __forceinline__ void stage_zero(uint8_t *stage, int bytes) {
-    for (int k = threadIdx.x * 16; k < bytes; k += kThreads * 16)
-        *reinterpret_cast<u32x4 *>(stage + k) = u32x4{0, 0, 0, 0};
-}
-
-// Write a unit's staged scales.  Swizzled: line g of each of the band's
-// tiles.  Linear: the unit's live rows, contiguous in the scale matrix.
-template <int LAYOUT>
-__device__ __forceinline__ void stage_flush(const uint8_t *stage, uint8_t *scales, int lu,
-                                            int live_rows, int sf_cols, int sf_stride) {
-    if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-        const int tiles = sf_stride >> 2;
-        uint8_t *dst = scales + ((int64_t)(lu >> 2) * tiles) * 512 + (lu & 3) * 128;
-        for (int k = threadIdx.x; k < tiles * 8; k += kThreads) {
-            const int t = k >> 3, part = k & 7;
-            *reinterpret_cast<u32x4 *>(dst + (int64_t)t * 512 + part * 16) =
-                *reinterpret_cast<const u32x4 *>(stage + t * 128 + part * 16);
-        }
+// Copy n staged bytes to global memory (any alignment of dst).
+__device__ __forceinline__ void copy_out(uint8_t *dst, const uint8_t *src, int n) {
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        const int nv = n >> 4;
+        for (int k = threadIdx.x; k < nv; k += kThreads)
+            *reinterpret_cast<u32x4 *>(dst + k * 16) = *reinterpret_cast<const u32x4 *>(src + k * 16);
+        for (int k = (nv << 4) + threadIdx.x; k < n; k += kThreads) dst[k] = src[k];
     } else {
-        const int n = live_rows * sf_cols;
-        uint8_t *dst = scales + (int64_t)lu * kUnitRows * sf_cols;
-        if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-            const int nv = n >> 4;
-            for (int k = threadIdx.x; k < nv; k += kThreads)
-                *reinterpret_cast<u32x4 *>(dst + k * 16) =
-                    *reinterpret_cast<const u32x4 *>(stage + k * 16);
-            for (int k = (nv << 4) + threadIdx.x; k < n; k += kThreads) dst[k] = stage[k];
-        } else {
-            for (int k = threadIdx.x; k < n; k += kThreads) dst[k] = stage[k];
-        }
-    }
-}
-
-// Quantize the rows of one unit (wave q's 8 rows), staging scales.
-// rows: live rows of the tensor; src/payload point at row 0.
-template <int FMT, int LAYOUT, bool kRowAmax>
-__device__ __forceinline__ void quant_unit_rows(const uint16_t *src, int64_t ld, uint8_t *payload,
-                                                int64_t payload_ld, int rows, int cols, int lu,
-                                                float g, uint8_t *stage, int sf_stride,
-                                                float *row_amax) {
-    using Tr = FmtTraits<FMT>;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int q = threadIdx.x >> 6;
-    uint32_t amax_row[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax_row[i] = 0;
-
-    for (int c0 = 0; c0 < cols; c0 += kChunk) {
-        const int col = c0 + lane * 8;
-        const bool live_col = col < cols;
-        u32x4 v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = unit_row<LAYOUT>(lu, q, i);
-            if (r < rows && live_col)
-                v[i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4 *>(src + (int64_t)r * ld + col));
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = unit_row<LAYOUT>(lu, q, i);
-            if (r < rows && live_col) {
-                u32x2 pay;
-                const uint32_t code = quant8<FMT>(v[i], g, pay);
-                store_payload<FMT>(payload + (int64_t)r * payload_ld, col, pay);
-                if ((lane & (Tr::kLanesPerBlock - 1)) == 0)
-                    stage[stage_index<LAYOUT>(q, i, col / Tr::kBlock, sf_stride)] = (uint8_t)code;
-                if constexpr (kRowAmax) amax_row[i] = max(amax_row[i], amax_bits8(v[i]));
-            }
-        }
-    }
-    if constexpr (kRowAmax) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = unit_row<LAYOUT>(lu, q, i);
-            if (r < rows) {
-                const uint32_t m = wave_max(amax_row[i]);
-                if (lane == 0) row_amax[r] = __uint_as_float(m << 16);
-            }
-        }
+        for (int k = threadIdx.x; k < n; k += kThreads) dst[k] = src[k];
     }
 }
 
 // ---------------------------------------------------------------------------
 // Grouped: 1..16 experts, one launch, the descriptor table in kernel args.
 // ---------------------------------------------------------------------------
+template <int LAYOUT>
+__device__ __forceinline__ int group_row(int rg, int q, int i) {
+    if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+        return (rg >> 2) * 128 + 32 * q + 8 * (rg & 3) + i;
+    else
+        return rg * kUnitRows + 8 * q + i;
+}
+
 template <int FMT, int LAYOUT>
 __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
-    extern __shared__ __align__(16) uint8_t stage[];
-    const int stage_bytes = kUnitRows * a.sf_stride;
+    using Tr = FmtTraits<FMT>;
+    constexpr int kCodes = kChunk / Tr::kBlock;  // scale codes per row per unit: 16 or 32
+    __shared__ __align__(16) uint8_t stage[kUnitRows * kCodes];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = threadIdx.x >> 6;
+    const int cl = lane * 8 / Tr::kBlock;  // this lane's code column inside the unit
+    const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
-    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
+    for (int b = blockIdx.x; b < a.total_units; b += gridDim.x) {
+        const int u = (int)gridDim.x == a.total_units ? xcd_unit(b, a.total_units) : b;
         int ei = 0;
         while (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) ++ei;
         const GEntry &E = a.e[ei];
         const int lu = u - E.unit_begin;
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) stage_zero(stage, stage_bytes);
-        __syncthreads();
+        const int rg = lu / a.n_cc;
+        const int cc = lu - rg * a.n_cc;
+        const int col = cc * kChunk + lane * 8;
+        const bool live_col = col < a.cols;
         const float g = FMT == MXQ_NVFP4 ? *E.g : 0.0f;
-        quant_unit_rows<FMT, LAYOUT, false>(E.src, E.ld, E.payload, payload_ld, E.rows, a.cols, lu,
-                                            g, stage, a.sf_stride, nullptr);
+
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = group_row<LAYOUT>(rg, q, i);
+            if (r < E.rows && live_col)
+                v[i] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4 *>(E.src + (int64_t)r * E.ld + col));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = group_row<LAYOUT>(rg, q, i);
+            uint32_t code = 0;  // rows and columns past the tensor stage zeros
+            if (r < E.rows && live_col) {
+                u32x2 pay;
+                code = quant8<FMT>(v[i], g, pay);
+                store_payload<FMT>(E.payload + (int64_t)r * payload_ld, col, pay);
+            }
+            if (leader) {
+                if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+                    stage[(cl >> 2) * 128 + i * 16 + q * 4 + (cl & 3)] = (uint8_t)code;
+                else
+                    stage[(8 * q + i) * kCodes + cl] = (uint8_t)code;
+            }
+        }
         __syncthreads();
-        stage_flush<LAYOUT>(stage, E.scales, lu, min(kUnitRows, E.rows - lu * kUnitRows),
-                            a.sf_cols, a.sf_stride);
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            // line g of each tile this chunk touches: (kCodes/4) tiles x 8 x 16 bytes
+            const int tiles = a.sf_stride >> 2;
+            const int t0 = cc * (kCodes / 4);
+            const int k = threadIdx.x;
+            if (k < (kCodes / 4) * 8) {
+                const int tl = k >> 3, part = k & 7;
+                if (t0 + tl < tiles) {
+                    uint8_t *dst = E.scales + ((int64_t)(rg >> 2) * tiles + t0 + tl) * 512 +
+                                   (rg & 3) * 128 + part * 16;
+                    *reinterpret_cast<u32x4 *>(dst) =
+                        *reinterpret_cast<const u32x4 *>(stage + tl * 128 + part * 16);
+                }
+            }
+        } else {
+            const int c0 = cc * kCodes;
+            const int ncodes = min(kCodes, a.sf_cols - c0);
+            constexpr int kParts = kCodes / 16;
+            for (int k = threadIdx.x; k < kUnitRows * kParts; k += kThreads) {
+                const int rl = k / kParts, part = k % kParts;
+                const int r = rg * kUnitRows + rl;
+                if (r >= E.rows) continue;
+                uint8_t *dst = E.scales + (int64_t)r * a.sf_cols + c0 + part * 16;
+                const uint8_t *src = stage + rl * kCodes + part * 16;
+                if (ncodes == kCodes && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                    *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+                } else {
+                    for (int j = 0; j < 16 && part * 16 + j < ncodes; ++j) dst[j] = src[j];
+                }
+            }
+        }
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// Split: one concatenated activation, per-expert units and scale regions.
+// Row-per-wave units (split, fused): 4 rows per workgroup, one per wave.
+// Staged scales: swizzled [tile][wave][4] (16 bytes per tile), linear
+// [wave][C].
 // ---------------------------------------------------------------------------
 template <int LAYOUT>
+__device__ __forceinline__ int wave_row(int lu, int q) {
+    if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+        return (lu >> 5) * 128 + 32 * q + (lu & 31);
+    else
+        return lu * 4 + q;
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void stage_code(uint8_t *stage, int q, int c, int sf_cols,
+                                           uint32_t code) {
+    if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+        stage[(c >> 2) * 16 + q * 4 + (c & 3)] = (uint8_t)code;
+    else
+        stage[q * sf_cols + c] = (uint8_t)code;
+}
+
+// Write a 4-row unit's staged scales into a scale matrix region of `rows` rows.
+template <int LAYOUT>
+__device__ __forceinline__ void flush_rows4(const uint8_t *stage, uint8_t *region, int lu,
+                                            int rows, int sf_cols, int sf_stride) {
+    if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+        const int tiles = sf_stride >> 2;
+        uint8_t *base = region + (int64_t)(lu >> 5) * tiles * 512 + (lu & 31) * 16;
+        for (int t = threadIdx.x; t < tiles; t += kThreads)
+            *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512) =
+                *reinterpret_cast<const u32x4 *>(stage + t * 16);
+    } else {
+        const int live = min(4, rows - lu * 4);
+        copy_out(region + (int64_t)lu * 4 * sf_cols, stage, live * sf_cols);
+    }
+}
+
+// Split: quantize rows of one expert's slice; NCH 512-column steps per row.
+template <int LAYOUT, int NCH>
 __global__ __launch_bounds__(kThreads) void k_split(const SplitArgs a) {
     extern __shared__ __align__(16) uint8_t stage[];
-    const int stage_bytes = kUnitRows * a.sf_stride;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = threadIdx.x >> 6;
     const int64_t payload_ld = a.cols / 2;
     const float g = *a.g;
-    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
-        // split s with unit_off[s] <= u < unit_off[s+1] (binary search)
-        int lo = 0, hi = a.n;
+    for (int b = blockIdx.x; b < a.total_units; b += gridDim.x) {
+        const int u = (int)gridDim.x == a.total_units ? xcd_unit(b, a.total_units) : b;
+        int lo = 0, hi = a.n;  // split s with unit_off[s] <= u < unit_off[s + 1]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (a.unit_off[mid] <= u) lo = mid; else hi = mid;
@@ -204,50 +241,63 @@ __global__ __launch_bounds__(kThreads) void k_split(const SplitArgs a) {
         const int lu = u - a.unit_off[s];
         const int m = a.row_off[s + 1] - a.row_off[s];
         const int64_t r0 = a.row_off[s];
-        uint8_t *scales = LAYOUT == MXQ_SF_SWIZZLED
-                              ? a.scales + (int64_t)a.unit_off[s] * kUnitRows * a.sf_stride
+        const int r = wave_row<LAYOUT>(lu, q);
+        if (r < m) {
+            const uint16_t *src = a.src + (r0 + r) * a.cols;
+            u32x4 v[NCH];
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) {
+                const int col = ch * kChunk + lane * 8;
+                if (col < a.cols)
+                    v[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + col));
+            }
+            uint8_t *pay_row = a.payload + (r0 + r) * payload_ld;
+            uint32_t amax = 0;
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) {
+                const int col = ch * kChunk + lane * 8;
+                if (col < a.cols) {
+                    u32x2 pay;
+                    const uint32_t code = quant8<MXQ_NVFP4>(v[ch], g, pay);
+                    store_payload<MXQ_NVFP4>(pay_row, col, pay);
+                    amax = max(amax, amax_bits8(v[ch]));
+                    if ((lane & 1) == 0) stage_code<LAYOUT>(stage, q, col / 16, a.sf_cols, code);
+                } else if ((lane & 1) == 0 && col / 16 < a.sf_stride) {
+                    stage_code<LAYOUT>(stage, q, col / 16, a.sf_cols, 0);
+                }
+            }
+            amax = wave_max(amax);
+            if (a.row_amax && lane == 0) a.row_amax[r0 + r] = __uint_as_float(amax << 16);
+        } else if (LAYOUT == MXQ_SF_SWIZZLED) {
+            for (int c = lane; c < a.sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, a.sf_cols, 0);
+        }
+        __syncthreads();
+        uint8_t *region = LAYOUT == MXQ_SF_SWIZZLED
+                              ? a.scales + (int64_t)a.unit_off[s] * 4 * a.sf_stride
                               : a.scales + r0 * a.sf_cols;
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) stage_zero(stage, stage_bytes);
-        __syncthreads();
-        if (a.row_amax)
-            quant_unit_rows<MXQ_NVFP4, LAYOUT, true>(a.src + r0 * a.cols, a.cols,
-                                                     a.payload + r0 * payload_ld, payload_ld, m,
-                                                     a.cols, lu, g, stage, a.sf_stride,
-                                                     a.row_amax + r0);
-        else
-            quant_unit_rows<MXQ_NVFP4, LAYOUT, false>(a.src + r0 * a.cols, a.cols,
-                                                      a.payload + r0 * payload_ld, payload_ld, m,
-                                                      a.cols, lu, g, stage, a.sf_stride, nullptr);
-        __syncthreads();
-        stage_flush<LAYOUT>(stage, scales, lu, min(kUnitRows, m - lu * kUnitRows), a.sf_cols,
-                            a.sf_stride);
+        flush_rows4<LAYOUT>(stage, region, lu, m, a.sf_cols, a.sf_stride);
         __syncthreads();
     }
 }
 
-// ---------------------------------------------------------------------------
-// Fused residual add + RMSNorm + quantize.  A wave owns whole rows: it keeps
-// the row's bf16 residual sum in registers (NCH 512-element steps), reduces
-// the sum of squares across the wave in a fixed order, then writes norm_out
-// and quantizes the same bf16 values.
-// ---------------------------------------------------------------------------
+// Fused residual add + RMSNorm + quantize, one row per wave.  The row's bf16
+// residual sum stays in registers; the sum of squares is reduced across the
+// wave in a fixed order; norm_out and the quantized form come from the same
+// bf16 values.
 template <int FMT, int LAYOUT, int NCH>
 __global__ __launch_bounds__(kThreads) void k_fused(const FusedArgs a) {
     using Tr = FmtTraits<FMT>;
     extern __shared__ __align__(16) uint8_t stage[];
-    const int stage_bytes = kUnitRows * a.sf_stride;
     const int lane = threadIdx.x & (kWave - 1);
     const int q = threadIdx.x >> 6;
     const int H = a.H;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
     const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
-    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
-        const int lu = u;
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) stage_zero(stage, stage_bytes);
-        __syncthreads();
-        for (int i = 0; i < 8; ++i) {
-            const int r = unit_row<LAYOUT>(lu, q, i);
-            if (r >= a.T) continue;  // uniform across the wave
+    const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
+    for (int b = blockIdx.x; b < a.total_units; b += gridDim.x) {
+        const int lu = (int)gridDim.x == a.total_units ? xcd_unit(b, a.total_units) : b;
+        const int r = wave_row<LAYOUT>(lu, q);
+        if (r < a.T) {
             const int64_t rb = (int64_t)r * H;
             u32x4 xv[NCH], rv[NCH];
 #pragma unroll
@@ -274,37 +324,40 @@ __global__ __launch_bounds__(kThreads) void k_fused(const FusedArgs a) {
                         acc = __builtin_fmaf(fhi, fhi, acc);
                         sum[j] = blo | (bhi << 16);
                     }
-                    xv[ch] = sum;  // keep the bf16 residual sum
+                    xv[ch] = sum;  // the bf16 residual sum
                     *reinterpret_cast<u32x4 *>(a.res_out + rb + col) = sum;
                 }
             }
-            const float ss = wave_sum(acc);
-            const float inv = 1.0f / __builtin_sqrtf(ss / (float)H + a.eps);
+            const float inv = 1.0f / __builtin_sqrtf(wave_sum(acc) / (float)H + a.eps);
+            u32x4 gm[NCH];
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) {
+                const int col = ch * kChunk + lane * 8;
+                if (col < H) gm[ch] = *reinterpret_cast<const u32x4 *>(a.gamma + col);
+            }
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch) {
                 const int col = ch * kChunk + lane * 8;
                 if (col < H) {
-                    const u32x4 gm = *reinterpret_cast<const u32x4 *>(a.gamma + col);
                     u32x4 nv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float nlo = (bf16_lo(xv[ch][j]) * bf16_lo(gm[j])) * inv;
-                        const float nhi = (bf16_hi(xv[ch][j]) * bf16_hi(gm[j])) * inv;
+                        const float nlo = (bf16_lo(xv[ch][j]) * bf16_lo(gm[ch][j])) * inv;
+                        const float nhi = (bf16_hi(xv[ch][j]) * bf16_hi(gm[ch][j])) * inv;
                         nv[j] = pack_bf16(nlo, nhi);
                     }
                     *reinterpret_cast<u32x4 *>(a.norm_out + rb + col) = nv;
                     u32x2 pay;
                     const uint32_t code = quant8<FMT>(nv, g, pay);
                     store_payload<FMT>(a.payload + (int64_t)r * payload_ld, col, pay);
-                    if ((lane & (Tr::kLanesPerBlock - 1)) == 0)
-                        stage[stage_index<LAYOUT>(q, i, col / Tr::kBlock, a.sf_stride)] =
-                            (uint8_t)code;
+                    if (leader) stage_code<LAYOUT>(stage, q, col / Tr::kBlock, a.sf_cols, code);
                 }
             }
+        } else if (LAYOUT == MXQ_SF_SWIZZLED) {
+            for (int c = lane; c < a.sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, a.sf_cols, 0);
         }
         __syncthreads();
-        stage_flush<LAYOUT>(stage, a.scales, lu, min(kUnitRows, a.T - lu * kUnitRows), a.sf_cols,
-                            a.sf_stride);
+        flush_rows4<LAYOUT>(stage, a.scales, lu, a.T, a.sf_cols, a.sf_stride);
         __syncthreads();
     }
 }
@@ -342,47 +395,67 @@ __global__ __launch_bounds__(kThreads) void k_swizzle(const SwizzleArgs a) {
 static inline unsigned grid_of(int64_t g) { return (unsigned)(g < 1 ? 1 : g); }
 
 hipError_t launch_grouped(int fmt, int layout, const GroupArgs &a, int64_t grid, hipStream_t s) {
-    const size_t lds = (size_t)kUnitRows * a.sf_stride;
     const dim3 gd(grid_of(grid)), bd(kThreads);
     if (fmt == MXQ_MXFP8 && layout == MXQ_SF_LINEAR)
-        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_LINEAR>), gd, bd, lds, s, a);
+        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_LINEAR>), gd, bd, 0, s, a);
     else if (fmt == MXQ_MXFP8)
-        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_SWIZZLED>), gd, bd, lds, s, a);
+        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_SWIZZLED>), gd, bd, 0, s, a);
     else if (layout == MXQ_SF_LINEAR)
-        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_LINEAR>), gd, bd, lds, s, a);
+        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_LINEAR>), gd, bd, 0, s, a);
     else
-        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_SWIZZLED>), gd, bd, lds, s, a);
+        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_SWIZZLED>), gd, bd, 0, s, a);
     return hipGetLastError();
 }
 
+// Row-per-wave kernels keep the whole row in registers: NCH 512-column steps.
+int row_steps(int64_t cols) {
+    const int64_t n = (cols + kChunk - 1) / kChunk;
+    if (n <= 2) return 2;
+    if (n <= 4) return 4;
+    if (n <= 8) return 8;
+    if (n <= 14) return 14;
+    if (n <= 16) return 16;
+    return 32;
+}
+
+template <int LAYOUT>
+static void split_nch(const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
+    const dim3 bd(kThreads);
+    switch (row_steps(a.cols)) {
+    case 2: hipLaunchKernelGGL((k_split<LAYOUT, 2>), gd, bd, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_split<LAYOUT, 4>), gd, bd, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_split<LAYOUT, 8>), gd, bd, lds, s, a); break;
+    case 14: hipLaunchKernelGGL((k_split<LAYOUT, 14>), gd, bd, lds, s, a); break;
+    case 16: hipLaunchKernelGGL((k_split<LAYOUT, 16>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_split<LAYOUT, 32>), gd, bd, lds, s, a); break;
+    }
+}
+
 hipError_t launch_split(int layout, const SplitArgs &a, int64_t grid, hipStream_t s) {
-    const size_t lds = (size_t)kUnitRows * a.sf_stride;
-    const dim3 gd(grid_of(grid)), bd(kThreads);
+    const size_t lds = (size_t)4 * a.sf_stride;
+    const dim3 gd(grid_of(grid));
     if (layout == MXQ_SF_LINEAR)
-        hipLaunchKernelGGL((k_split<MXQ_SF_LINEAR>), gd, bd, lds, s, a);
+        split_nch<MXQ_SF_LINEAR>(a, gd, lds, s);
     else
-        hipLaunchKernelGGL((k_split<MXQ_SF_SWIZZLED>), gd, bd, lds, s, a);
+        split_nch<MXQ_SF_SWIZZLED>(a, gd, lds, s);
     return hipGetLastError();
 }
 
 template <int FMT, int LAYOUT>
 static void fused_nch(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
-    const int nch = (a.H + kChunk - 1) / kChunk;
     const dim3 bd(kThreads);
-    if (nch <= 2)
-        hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 2>), gd, bd, lds, s, a);
-    else if (nch <= 4)
-        hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 4>), gd, bd, lds, s, a);
-    else if (nch <= 8)
-        hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 8>), gd, bd, lds, s, a);
-    else if (nch <= 16)
-        hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16>), gd, bd, lds, s, a);
-    else
-        hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 32>), gd, bd, lds, s, a);
+    switch (row_steps(a.H)) {
+    case 2: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 2>), gd, bd, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 4>), gd, bd, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 8>), gd, bd, lds, s, a); break;
+    case 14: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 14>), gd, bd, lds, s, a); break;
+    case 16: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 32>), gd, bd, lds, s, a); break;
+    }
 }
 
 hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s) {
-    const size_t lds = (size_t)kUnitRows * a.sf_stride;
+    const size_t lds = (size_t)4 * a.sf_stride;
     const dim3 gd(grid_of(grid));
     if (fmt == MXQ_MXFP8 && layout == MXQ_SF_LINEAR)
         fused_nch<MXQ_MXFP8, MXQ_SF_LINEAR>(a, gd, lds, s);
