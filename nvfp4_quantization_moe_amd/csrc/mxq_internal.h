@@ -11,7 +11,8 @@
 namespace mxq {
 
 constexpr int kThreads = 256;  // 4 waves per workgroup
-constexpr int kUnitRows = 32;  // rows per grouped work unit (8 per wave)
+constexpr int kRowsPerWave = 4;                // rows per wave in a grouped unit
+constexpr int kUnitRows = 4 * kRowsPerWave;   // rows per grouped work unit
 constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
 constexpr int kRowUnit = 4;    // rows per split/fused work unit (1 per wave)
 

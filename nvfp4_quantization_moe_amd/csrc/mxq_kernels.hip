@@ -6,20 +6,22 @@
 // workgroup issued before any of its stores, 16 contiguous bytes per lane
 // (a wave load is 1 KiB of one row), and each lane's output bytes contiguous.
 //
-// Grouped (k_grouped): a work unit is 32 rows x 512 columns of one expert,
-// 8 rows per wave.  A block of 32 (MXFP8) or 16 (NVFP4) elements spans 4 or 2
+// Grouped (k_grouped): a work unit is 4*kRowsPerWave rows x 512 columns of
+// one expert, kRowsPerWave rows per wave.  A block of 32 (MXFP8) or 16 (NVFP4) elements spans 4 or 2
 // adjacent lanes; its amax is reduced with DPP quad permutes, never through
 // LDS.  Payload bytes go straight to HBM; scale bytes are staged in LDS.  With
-// the swizzled layout the unit's rows are band*128 + 32*wave + 8*g + i
-// (i = 0..7) of one 128-row band, which fill exactly one 128-byte line of each
-// 512-byte tile the chunk touches, so scales leave as whole lines, padding
-// included.
+// the swizzled layout the unit's rows are band*128 + 32*wave + R*h + i
+// (R = kRowsPerWave, i < R) of one 128-row band, which fill one contiguous
+// R*16-byte segment of each 512-byte tile the chunk touches (a whole 128-byte
+// line for R = 8), so scales leave in whole segments, padding included.
 //
 // Split and fused (k_split, k_fused): they need whole rows (row amax, the
 // RMSNorm sum of squares), so one wave owns one row and holds all of it in
-// registers; a unit is 4 rows.  Swizzled units take rows band*128 + 32*wave +
-// gi (gi = 0..31), so a unit writes one 16-byte piece of each tile line and
-// the 8 consecutive units that complete a line run on the same XCD.
+// registers; a unit is 4 rows.  Fused swizzled units take rows band*128 +
+// 32*wave + gi (gi = 0..31), so a unit writes one 16-byte piece of each tile
+// line and the 8 consecutive units that complete a line run on the same XCD.
+// Split units take 4 consecutive rows of one expert, so short experts keep
+// every wave busy.
 //
 // Units are assigned to workgroups XCD by XCD: hardware dispatches workgroup b
 // to XCD b mod 8, and unit order is remapped so that each XCD (with its own
@@ -65,12 +67,14 @@ __device__ __forceinline__ uint32_t quant8(u32x4 v, float g, u32x2 &pay) {
     }
 }
 
+// Payload bytes are written once and not read back by this kernel: streaming
+// (non-temporal) stores keep them from displacing cache lines.
 template <int FMT>
 __device__ __forceinline__ void store_payload(uint8_t *row_payload, int col, u32x2 pay) {
     if constexpr (FMT == MXQ_MXFP8)
-        *reinterpret_cast<u32x2 *>(row_payload + col) = pay;
+        __builtin_nontemporal_store(pay, reinterpret_cast<u32x2 *>(row_payload + col));
     else
-        *reinterpret_cast<uint32_t *>(row_payload + (col >> 1)) = pay.x;
+        __builtin_nontemporal_store(pay.x, reinterpret_cast<uint32_t *>(row_payload + (col >> 1)));
 }
 
 // Workgroup b -> unit, contiguous per XCD (bijective on [0, n)).
@@ -94,18 +98,22 @@ __device__ __forceinline__ void copy_out(uint8_t *dst, const uint8_t *src, int n
 // ---------------------------------------------------------------------------
 // Grouped: 1..16 experts, one launch, the descriptor table in kernel args.
 // ---------------------------------------------------------------------------
+// Row groups of a 128-row band (swizzled): 32 / kRowsPerWave.
+constexpr int kGroupsPerBand = 32 / kRowsPerWave;
+
 template <int LAYOUT>
 __device__ __forceinline__ int group_row(int rg, int q, int i) {
     if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-        return (rg >> 2) * 128 + 32 * q + 8 * (rg & 3) + i;
+        return (rg / kGroupsPerBand) * 128 + 32 * q + kRowsPerWave * (rg % kGroupsPerBand) + i;
     else
-        return rg * kUnitRows + 8 * q + i;
+        return rg * kUnitRows + kRowsPerWave * q + i;
 }
 
 template <int FMT, int LAYOUT>
 __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
     using Tr = FmtTraits<FMT>;
     constexpr int kCodes = kChunk / Tr::kBlock;  // scale codes per row per unit: 16 or 32
+    constexpr int kSegBytes = kRowsPerWave * 16;   // bytes of one tile line the unit fills
     __shared__ __align__(16) uint8_t stage[kUnitRows * kCodes];
     const int lane = threadIdx.x & (kWave - 1);
     const int q = threadIdx.x >> 6;
@@ -124,16 +132,16 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
         const bool live_col = col < a.cols;
         const float g = FMT == MXQ_NVFP4 ? *E.g : 0.0f;
 
-        u32x4 v[8];
+        u32x4 v[kRowsPerWave];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kRowsPerWave; ++i) {
             const int r = group_row<LAYOUT>(rg, q, i);
             if (r < E.rows && live_col)
                 v[i] = __builtin_nontemporal_load(
                     reinterpret_cast<const u32x4 *>(E.src + (int64_t)r * E.ld + col));
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kRowsPerWave; ++i) {
             const int r = group_row<LAYOUT>(rg, q, i);
             uint32_t code = 0;  // rows and columns past the tensor stage zeros
             if (r < E.rows && live_col) {
@@ -143,24 +151,26 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
             }
             if (leader) {
                 if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-                    stage[(cl >> 2) * 128 + i * 16 + q * 4 + (cl & 3)] = (uint8_t)code;
+                    stage[(cl >> 2) * kSegBytes + i * 16 + q * 4 + (cl & 3)] = (uint8_t)code;
                 else
-                    stage[(8 * q + i) * kCodes + cl] = (uint8_t)code;
+                    stage[(kRowsPerWave * q + i) * kCodes + cl] = (uint8_t)code;
             }
         }
         __syncthreads();
         if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-            // line g of each tile this chunk touches: (kCodes/4) tiles x 8 x 16 bytes
+            // the unit's segment of each tile this chunk touches:
+            // (kCodes/4) tiles x kRowsPerWave x 16 bytes
             const int tiles = a.sf_stride >> 2;
             const int t0 = cc * (kCodes / 4);
             const int k = threadIdx.x;
-            if (k < (kCodes / 4) * 8) {
-                const int tl = k >> 3, part = k & 7;
+            if (k < (kCodes / 4) * kRowsPerWave) {
+                const int tl = k / kRowsPerWave, part = k % kRowsPerWave;
                 if (t0 + tl < tiles) {
-                    uint8_t *dst = E.scales + ((int64_t)(rg >> 2) * tiles + t0 + tl) * 512 +
-                                   (rg & 3) * 128 + part * 16;
+                    uint8_t *dst = E.scales +
+                                   ((int64_t)(rg / kGroupsPerBand) * tiles + t0 + tl) * 512 +
+                                   (rg % kGroupsPerBand) * kSegBytes + part * 16;
                     *reinterpret_cast<u32x4 *>(dst) =
-                        *reinterpret_cast<const u32x4 *>(stage + tl * 128 + part * 16);
+                        *reinterpret_cast<const u32x4 *>(stage + tl * kSegBytes + part * 16);
                 }
             }
         } else {
@@ -222,6 +232,21 @@ __device__ __forceinline__ void flush_rows4(const uint8_t *stage, uint8_t *regio
     }
 }
 
+// Split units are 4 consecutive rows of one expert (short experts would leave
+// waves idle under the interleaved order).  Swizzled scales of such a unit
+// form one dword per row in each tile.
+__device__ __forceinline__ void flush_split_swz(const uint8_t *stage, uint8_t *region, int lu,
+                                                int sf_stride) {
+    const int tiles = sf_stride >> 2;
+    const int r0 = lu * 4;
+    uint8_t *base = region + (int64_t)(r0 >> 7) * tiles * 512 + ((r0 & 127) >> 5) * 4;
+    for (int k = threadIdx.x; k < tiles * 4; k += kThreads) {
+        const int t = k >> 2, qq = k & 3;
+        *reinterpret_cast<uint32_t *>(base + (int64_t)t * 512 + ((r0 & 31) + qq) * 16) =
+            *reinterpret_cast<const uint32_t *>(stage + t * 16 + qq * 4);
+    }
+}
+
 // Split: quantize rows of one expert's slice; NCH 512-column steps per row.
 template <int LAYOUT, int NCH>
 __global__ __launch_bounds__(kThreads) void k_split(const SplitArgs a) {
@@ -241,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void k_split(const SplitArgs a) {
         const int lu = u - a.unit_off[s];
         const int m = a.row_off[s + 1] - a.row_off[s];
         const int64_t r0 = a.row_off[s];
-        const int r = wave_row<LAYOUT>(lu, q);
+        const int r = lu * 4 + q;
         if (r < m) {
             const uint16_t *src = a.src + (r0 + r) * a.cols;
             u32x4 v[NCH];
@@ -272,10 +297,11 @@ __global__ __launch_bounds__(kThreads) void k_split(const SplitArgs a) {
             for (int c = lane; c < a.sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, a.sf_cols, 0);
         }
         __syncthreads();
-        uint8_t *region = LAYOUT == MXQ_SF_SWIZZLED
-                              ? a.scales + (int64_t)a.unit_off[s] * 4 * a.sf_stride
-                              : a.scales + r0 * a.sf_cols;
-        flush_rows4<LAYOUT>(stage, region, lu, m, a.sf_cols, a.sf_stride);
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+            flush_split_swz(stage, a.scales + (int64_t)a.unit_off[s] * 4 * a.sf_stride, lu,
+                            a.sf_stride);
+        else
+            flush_rows4<LAYOUT>(stage, a.scales + r0 * a.sf_cols, lu, m, a.sf_cols, a.sf_stride);
         __syncthreads();
     }
 }
