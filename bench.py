@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--cpu-experts", type=int, default=16,
+    ap.add_argument("--cpu-experts", type=int, default=32,
                     help="gate_up experts in the CPU oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (hardware-counter calibration)")
@@ -283,6 +283,7 @@ def cpu_baseline(torch, gate_up, n_experts):
     import numpy as np
     import oracle
     oracle.lib()
+    n_experts = min(n_experts, gate_up.shape[0])
     host = gate_up[:n_experts].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     rows, cols = host.shape[1], host.shape[2]
     t0 = time.perf_counter()

@@ -19,15 +19,18 @@
 // RMSNorm sum of squares), so one wave owns one row and holds all of it in
 // registers; a unit is 4 rows.  Fused swizzled units take rows band*128 +
 // 32*wave + gi (gi = 0..31), so a unit writes one 16-byte piece of each tile
-// line and the 8 consecutive units that complete a line run on the same XCD.
+// line (8 consecutive units complete it).
 // Split units take 4 consecutive rows of one expert, so short experts keep
 // every wave busy.
 //
-// Units are assigned to workgroups XCD by XCD: hardware dispatches workgroup b
-// to XCD b mod 8, and unit order is remapped so that each XCD (with its own
-// L2) walks a contiguous range of units.  No atomics, no scratch, no
-// inter-workgroup ordering: every byte has one writer, and the bytes do not
-// depend on the grid size.
+// Grouped and fused: unit u runs on workgroup u, in plain dispatch order; the
+// hardware spreads consecutive workgroups over the 8 XCDs, so the units in
+// flight cover one contiguous stretch of every tensor (measured faster than
+// giving each XCD a contiguous range).  Split: each XCD takes a contiguous
+// range of units, so the 4-row units that share a scale-tile line write it
+// through the same L2 (measured twice as fast there).  No atomics, no scratch, no inter-workgroup
+// ordering: every byte has one writer, and the bytes do not depend on the grid
+// size.
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
@@ -77,7 +80,8 @@ __device__ __forceinline__ void store_payload(uint8_t *row_payload, int col, u32
         __builtin_nontemporal_store(pay.x, reinterpret_cast<uint32_t *>(row_payload + (col >> 1)));
 }
 
-// Workgroup b -> unit, contiguous per XCD (bijective on [0, n)).
+// Workgroup b -> unit such that each XCD (workgroup b runs on XCD b mod 8)
+// walks a contiguous range of units; bijective on [0, n).
 __device__ __forceinline__ int xcd_unit(int b, int n) {
     const int q = n >> 3, r = n & 7, x = b & 7;
     return x * q + min(x, r) + (b >> 3);
@@ -120,8 +124,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
     const int cl = lane * 8 / Tr::kBlock;  // this lane's code column inside the unit
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
-    for (int b = blockIdx.x; b < a.total_units; b += gridDim.x) {
-        const int u = (int)gridDim.x == a.total_units ? xcd_unit(b, a.total_units) : b;
+    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
         int ei = 0;
         while (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) ++ei;
         const GEntry &E = a.e[ei];
@@ -320,8 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(const FusedArgs a) {
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
     const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
-    for (int b = blockIdx.x; b < a.total_units; b += gridDim.x) {
-        const int lu = (int)gridDim.x == a.total_units ? xcd_unit(b, a.total_units) : b;
+    for (int lu = blockIdx.x; lu < a.total_units; lu += gridDim.x) {
         const int r = wave_row<LAYOUT>(lu, q);
         if (r < a.T) {
             const int64_t rb = (int64_t)r * H;
