@@ -24,6 +24,34 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3_235b_layer.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    d = os.path.join(ROOT, "nvfp4_quantization_moe_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a device copy), or None
+    when the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k["traffic_bytes_per_launch"]
 
 
 def log(*a):
@@ -147,7 +175,7 @@ def main():
     achieved = dd["bytes"] / (dd["ms"] * 1e-3) / 1e9
     roofline = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(names[dom]),
                 "alg_bytes_per_launch": dd["bytes"] // dd["n"],
                 "avg_launch_us": round(dd["ms"] * 1e3 / dd["n"], 2)}
     log(f"[bench] step {ms_per_step:.3f} ms, {value:.1f} GB/s; dominant {names[dom]} "

@@ -154,7 +154,8 @@ int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols, const i
             a.row_off[j] = (int32_t)rows;
             a.unit_off[j] = (int32_t)units;
             rows += m;
-            units += row_groups(m, layout, kRowUnit);
+            // swizzled: 4 line-sets per 128-row band; linear: 32-row groups
+            units += layout == MXQ_SF_SWIZZLED ? (m + 127) / 128 * 4 : (m + 31) / 32;
             sbytes += sf_bytes(m, C, layout);
         }
         a.row_off[n] = (int32_t)rows;

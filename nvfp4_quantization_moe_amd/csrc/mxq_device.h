@@ -138,10 +138,25 @@ __device__ __forceinline__ float div6(float a) {
     return __builtin_fmaf(r, r6, q);
 }
 
-// s = fp32(fp32(amax / 6) * g); code = E4M3(s), saturating at 448; multiplier
-// fp32(g / decode(code)) (IEEE division), zero when the decoded scale is zero
-// or the multiplier is not a normal fp32 number.
-__device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g) {
+// Element multipliers for every possible block-scale code: mult[k] =
+// fp32(g / decode(k)) (IEEE division), zero when decode(k) is zero or the
+// quotient is not a normal fp32 number.  Block-scale codes are 0..126 (the
+// block scale is non-negative and saturates at 448 = code 126).  Filled by
+// threads 0..126 of a workgroup; the caller synchronizes before use.
+constexpr int kNvCodes = 127;
+__device__ __forceinline__ void nv_fill_mult(float *mult, float g) {
+    const int k = threadIdx.x;
+    if (k < kNvCodes) {
+        const float sq = e4m3_decode_pos((uint32_t)k);
+        const float m = g / sq;
+        mult[k] = (sq == 0.0f || !(m >= 0x1p-126f)) ? 0.0f : m;
+    }
+}
+
+// s = fp32(fp32(amax / 6) * g); code = E4M3(s), saturating at 448.  The
+// element multiplier comes from the table above when one is given (mult !=
+// nullptr), else from the same IEEE division done in place.
+__device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g, const float *mult) {
     const float s = div6(__uint_as_float(amax_bits << 16)) * g;
     Nv4Scale r;
     // v_cvt_scalef32_pk_fp8_f32 (scale 1.0) rounds to nearest even and keeps
@@ -149,9 +164,13 @@ __device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g) {
     const v2s k = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, __builtin_fminf(s, 448.0f),
                                                            0.0f, 1.0f, false);
     r.code = __builtin_bit_cast(uint32_t, k) & 0xFFu;
-    const float sq = e4m3_decode_pos(r.code);
-    const float m = g / sq;
-    r.mult = (sq == 0.0f || !(m >= 0x1p-126f)) ? 0.0f : m;
+    if (mult) {
+        r.mult = mult[r.code];
+    } else {
+        const float sq = e4m3_decode_pos(r.code);
+        const float m = g / sq;
+        r.mult = (sq == 0.0f || !(m >= 0x1p-126f)) ? 0.0f : m;
+    }
     return r;
 }
 

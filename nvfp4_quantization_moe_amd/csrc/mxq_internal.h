@@ -14,7 +14,9 @@ constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kRowsPerWave = 4;                // rows per wave in a grouped unit
 constexpr int kUnitRows = 4 * kRowsPerWave;   // rows per grouped work unit
 constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
-constexpr int kRowUnit = 4;    // rows per split/fused work unit (1 per wave)
+constexpr int kRowUnit = 4;    // rows per split/fused work unit
+constexpr int kRowThreads = 512;  // fused workgroup: 8 waves, 2 per row
+constexpr int kSplitThreads = 512;  // split workgroup: 8 waves, 2 per row
 
 // One grouped-launch descriptor.  The whole table travels in the kernel
 // arguments, so a grouped call is one dispatch with no device-side table.
@@ -40,8 +42,9 @@ struct GroupArgs {
 
 constexpr int kMaxSplitsPerLaunch = 256;
 
-// Up to 256 consecutive splits of a concatenated activation.  Work units are
-// 4-row groups that never straddle two experts.
+// Up to 256 consecutive splits of a concatenated activation.  A work unit is
+// 32 rows of one expert (swizzled: the rows of one 128-row band that share
+// line h of every scale tile); units never straddle two experts.
 struct SplitArgs {
     const uint16_t *src;  // global row 0 of this launch's first split
     uint8_t *payload;     // same row

@@ -15,20 +15,18 @@
 // R*16-byte segment of each 512-byte tile the chunk touches (a whole 128-byte
 // line for R = 8), so scales leave in whole segments, padding included.
 //
-// Split and fused (k_split, k_fused): they need whole rows (row amax, the
-// RMSNorm sum of squares), so one wave owns one row and holds all of it in
-// registers; a unit is 4 rows.  Fused swizzled units take rows band*128 +
-// 32*wave + gi (gi = 0..31), so a unit writes one 16-byte piece of each tile
-// line (8 consecutive units complete it).
-// Split units take 4 consecutive rows of one expert, so short experts keep
-// every wave busy.
+// Fused (k_fused) needs whole rows (the RMSNorm sum of squares): two waves
+// own one row and hold it in registers; a unit is 4 rows.  Swizzled units take
+// rows band*128 + 32*q + gi (gi = 0..31), so a unit writes one 16-byte piece
+// of each tile line (8 consecutive units complete it).
+// Split (k_split): a unit owns one line of every scale tile of a 128-row band
+// of one expert and loads only that line-set's live rows, whole rows, two
+// waves per row.
 //
 // Grouped and fused: unit u runs on workgroup u, in plain dispatch order; the
 // hardware spreads consecutive workgroups over the 8 XCDs, so the units in
 // flight cover one contiguous stretch of every tensor (measured faster than
-// giving each XCD a contiguous range).  Split: each XCD takes a contiguous
-// range of units, so the 4-row units that share a scale-tile line write it
-// through the same L2 (measured twice as fast there).  No atomics, no scratch, no inter-workgroup
+// giving each XCD a contiguous range).  No global atomics, no scratch, no inter-workgroup
 // ordering: every byte has one writer, and the bytes do not depend on the grid
 // size.
 #include "mxq_device.h"
@@ -50,11 +48,13 @@ struct FmtTraits<MXQ_NVFP4> {
 };
 
 // Quantize one lane's 8 elements; the lanes of a block cooperate through DPP
-// (all lanes of a block must be active).  Returns the block's scale byte
+// (all lanes of a block must be active).  NVFP4 reads its element multiplier
+// from the workgroup's table (nv_fill_mult) or, with mult == nullptr,
+// divides in place (same quotient).  Returns the block's scale byte
 // (every lane of the block holds it) and the lane's payload: 8 bytes (MXFP8)
 // or 4 bytes in pay.x (NVFP4).
 template <int FMT>
-__device__ __forceinline__ uint32_t quant8(u32x4 v, float g, u32x2 &pay) {
+__device__ __forceinline__ uint32_t quant8(u32x4 v, float g, const float *mult, u32x2 &pay) {
     uint32_t a = amax_bits8(v);
     if constexpr (FMT == MXQ_MXFP8) {
         a = block_max4(a);
@@ -63,7 +63,7 @@ __device__ __forceinline__ uint32_t quant8(u32x4 v, float g, u32x2 &pay) {
         return c;
     } else {
         a = block_max2(a);
-        const Nv4Scale s = nv_scale(a, g);
+        const Nv4Scale s = nv_scale(a, g, mult);
         pay.x = nv_encode8(v, s.mult);
         pay.y = 0;
         return s.code;
@@ -78,25 +78,6 @@ __device__ __forceinline__ void store_payload(uint8_t *row_payload, int col, u32
         __builtin_nontemporal_store(pay, reinterpret_cast<u32x2 *>(row_payload + col));
     else
         __builtin_nontemporal_store(pay.x, reinterpret_cast<uint32_t *>(row_payload + (col >> 1)));
-}
-
-// Workgroup b -> unit such that each XCD (workgroup b runs on XCD b mod 8)
-// walks a contiguous range of units; bijective on [0, n).
-__device__ __forceinline__ int xcd_unit(int b, int n) {
-    const int q = n >> 3, r = n & 7, x = b & 7;
-    return x * q + min(x, r) + (b >> 3);
-}
-
-// Copy n staged bytes to global memory (any alignment of dst).
-__device__ __forceinline__ void copy_out(uint8_t *dst, const uint8_t *src, int n) {
-    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-        const int nv = n >> 4;
-        for (int k = threadIdx.x; k < nv; k += kThreads)
-            *reinterpret_cast<u32x4 *>(dst + k * 16) = *reinterpret_cast<const u32x4 *>(src + k * 16);
-        for (int k = (nv << 4) + threadIdx.x; k < n; k += kThreads) dst[k] = src[k];
-    } else {
-        for (int k = threadIdx.x; k < n; k += kThreads) dst[k] = src[k];
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -149,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
             uint32_t code = 0;  // rows and columns past the tensor stage zeros
             if (r < E.rows && live_col) {
                 u32x2 pay;
-                code = quant8<FMT>(v[i], g, pay);
+                code = quant8<FMT>(v[i], g, nullptr, pay);  // one unit: divide in place
                 store_payload<FMT>(E.payload + (int64_t)r * payload_ld, col, pay);
             }
             if (leader) {
@@ -198,18 +179,12 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row-per-wave units (split, fused): 4 rows per workgroup, one per wave.
-// Staged scales: swizzled [tile][wave][4] (16 bytes per tile), linear
-// [wave][C].
+// Whole-row units (split, fused): 4 rows per workgroup of 8 waves, two waves
+// per row; each wave holds half of its row in registers (512-column steps
+// 2k + half).  Row-wide reductions combine the two halves through LDS in a
+// fixed order.  Staged scales: swizzled [tile][row][4] (16 bytes per tile),
+// linear [row][C].
 // ---------------------------------------------------------------------------
-template <int LAYOUT>
-__device__ __forceinline__ int wave_row(int lu, int q) {
-    if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-        return (lu >> 5) * 128 + 32 * q + (lu & 31);
-    else
-        return lu * 4 + q;
-}
-
 template <int LAYOUT>
 __device__ __forceinline__ void stage_code(uint8_t *stage, int q, int c, int sf_cols,
                                            uint32_t code) {
@@ -219,47 +194,57 @@ __device__ __forceinline__ void stage_code(uint8_t *stage, int q, int c, int sf_
         stage[q * sf_cols + c] = (uint8_t)code;
 }
 
-// Write a 4-row unit's staged scales into a scale matrix region of `rows` rows.
+// Zero the staged codes of a row with no data (swizzled padding rows).
 template <int LAYOUT>
-__device__ __forceinline__ void flush_rows4(const uint8_t *stage, uint8_t *region, int lu,
-                                            int rows, int sf_cols, int sf_stride) {
-    if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-        const int tiles = sf_stride >> 2;
-        uint8_t *base = region + (int64_t)(lu >> 5) * tiles * 512 + (lu & 31) * 16;
-        for (int t = threadIdx.x; t < tiles; t += kThreads)
-            *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512) =
-                *reinterpret_cast<const u32x4 *>(stage + t * 16);
+__device__ __forceinline__ void stage_zero_row(uint8_t *stage, int q, int lane, int sf_cols,
+                                               int sf_stride) {
+    for (int c = lane; c < sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, sf_cols, 0);
+}
+
+// Copy n staged bytes to global memory with kRowThreads threads.
+__device__ __forceinline__ void copy_out_rows(uint8_t *dst, const uint8_t *src, int n) {
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        const int nv = n >> 4;
+        for (int k = threadIdx.x; k < nv; k += kRowThreads)
+            *reinterpret_cast<u32x4 *>(dst + k * 16) = *reinterpret_cast<const u32x4 *>(src + k * 16);
+        for (int k = (nv << 4) + threadIdx.x; k < n; k += kRowThreads) dst[k] = src[k];
     } else {
-        const int live = min(4, rows - lu * 4);
-        copy_out(region + (int64_t)lu * 4 * sf_cols, stage, live * sf_cols);
+        for (int k = threadIdx.x; k < n; k += kRowThreads) dst[k] = src[k];
     }
 }
 
-// Split units are 4 consecutive rows of one expert (short experts would leave
-// waves idle under the interleaved order).  Swizzled scales of such a unit
-// form one dword per row in each tile.
-__device__ __forceinline__ void flush_split_swz(const uint8_t *stage, uint8_t *region, int lu,
-                                                int sf_stride) {
+// Fused swizzled units take rows band*128 + 32*q + gi (gi = lu mod 32): one
+// 16-byte piece per tile line.
+__device__ __forceinline__ void flush_interleaved_swz(const uint8_t *stage, uint8_t *region,
+                                                      int lu, int sf_stride) {
     const int tiles = sf_stride >> 2;
-    const int r0 = lu * 4;
-    uint8_t *base = region + (int64_t)(r0 >> 7) * tiles * 512 + ((r0 & 127) >> 5) * 4;
-    for (int k = threadIdx.x; k < tiles * 4; k += kThreads) {
-        const int t = k >> 2, qq = k & 3;
-        *reinterpret_cast<uint32_t *>(base + (int64_t)t * 512 + ((r0 & 31) + qq) * 16) =
-            *reinterpret_cast<const uint32_t *>(stage + t * 16 + qq * 4);
-    }
+    uint8_t *base = region + (int64_t)(lu >> 5) * tiles * 512 + (lu & 31) * 16;
+    for (int t = threadIdx.x; t < tiles; t += kRowThreads)
+        *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512) =
+            *reinterpret_cast<const u32x4 *>(stage + t * 16);
 }
 
-// Split: quantize rows of one expert's slice; NCH 512-column steps per row.
-template <int LAYOUT, int NCH>
-__global__ __launch_bounds__(kThreads) void k_split(const SplitArgs a) {
+// Split.  Swizzled: a unit owns line h (0..3) of every scale tile of one
+// 128-row band of one expert, i.e. the rows band*128 + 32*q + 8*h + i
+// (q < 4, i < 8), so its staged scales leave as whole 128-byte lines, padding
+// rows and columns zero.  Linear: a unit is 32 consecutive rows.  Only the
+// unit's live rows are loaded: pairs of waves take them in turn, each wave
+// holding half of a row (512-column steps 2k + half) in registers, so short
+// experts keep every wave busy.  The row amax is the max over the two halves,
+// folded in LDS; no global atomics.
+template <int LAYOUT, int NCH2>
+__global__ __launch_bounds__(kSplitThreads) void k_split(const SplitArgs a) {
     extern __shared__ __align__(16) uint8_t stage[];
+    __shared__ uint32_t row_max[32];
+    __shared__ float mult[kNvCodes];
     const int lane = threadIdx.x & (kWave - 1);
-    const int q = threadIdx.x >> 6;
+    const int w = threadIdx.x >> 6;
+    const int pair = w >> 1, half = w & 1;
     const int64_t payload_ld = a.cols / 2;
     const float g = *a.g;
-    for (int b = blockIdx.x; b < a.total_units; b += gridDim.x) {
-        const int u = (int)gridDim.x == a.total_units ? xcd_unit(b, a.total_units) : b;
+    const int stage_bytes = 32 * a.sf_stride;
+    nv_fill_mult(mult, g);  // read after the first barrier below
+    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
         int lo = 0, hi = a.n;  // split s with unit_off[s] <= u < unit_off[s + 1]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -268,124 +253,206 @@ __global__ __launch_bounds__(kThreads) void k_split(const SplitArgs a) {
         const int s = lo;
         const int lu = u - a.unit_off[s];
         const int m = a.row_off[s + 1] - a.row_off[s];
-        const int64_t r0 = a.row_off[s];
-        const int r = lu * 4 + q;
-        if (r < m) {
-            const uint16_t *src = a.src + (r0 + r) * a.cols;
-            u32x4 v[NCH];
+        const int64_t e0 = a.row_off[s];  // expert's first row
+        // live rows of the unit, in order; nq[q] of them in line-set row q
+        int nq[4] = {0, 0, 0, 0};
+        int n_live;
+        int band = 0, h = 0;
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            band = lu >> 2;
+            h = lu & 3;
+            const int rb = min(128, m - band * 128);
+            n_live = 0;
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                const int col = ch * kChunk + lane * 8;
-                if (col < a.cols)
-                    v[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + col));
+            for (int q = 0; q < 4; ++q) {
+                nq[q] = min(8, max(0, rb - 32 * q - 8 * h));
+                n_live += nq[q];
             }
-            uint8_t *pay_row = a.payload + (r0 + r) * payload_ld;
+        } else {
+            n_live = min(32, m - lu * 32);
+        }
+        // j-th live row of the unit -> (line-set row q, slot i, row in expert)
+        auto locate = [&](int j, int &q, int &i) {
+            q = 0;
+            i = j;
+            if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+                while (i >= nq[q]) { i -= nq[q]; ++q; }
+                return band * 128 + 32 * q + 8 * h + i;
+            } else {
+                return lu * 32 + j;
+            }
+        };
+        auto load_row = [&](int j, u32x4 *v) {
+            int q, i;
+            const uint16_t *src = a.src + (e0 + locate(j, q, i)) * a.cols;
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
+                if (col < a.cols)
+                    v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + col));
+            }
+        };
+        u32x4 cur[NCH2], nxt[NCH2];
+        if (pair < n_live) load_row(pair, cur);
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            for (int k = threadIdx.x * 16; k < stage_bytes; k += kSplitThreads * 16)
+                *reinterpret_cast<u32x4 *>(stage + k) = u32x4{0, 0, 0, 0};
+        }
+        if (threadIdx.x < 32) row_max[threadIdx.x] = 0;
+        __syncthreads();
+        for (int j = pair; j < n_live; j += 4) {
+            if (j + 4 < n_live) load_row(j + 4, nxt);  // next row's loads in flight
+            int q, i;
+            const int r = locate(j, q, i);
+            uint8_t *pay_row = a.payload + (e0 + r) * payload_ld;
             uint32_t amax = 0;
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                const int col = ch * kChunk + lane * 8;
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
                 if (col < a.cols) {
                     u32x2 pay;
-                    const uint32_t code = quant8<MXQ_NVFP4>(v[ch], g, pay);
+                    const uint32_t code = quant8<MXQ_NVFP4>(cur[k], g, mult, pay);
                     store_payload<MXQ_NVFP4>(pay_row, col, pay);
-                    amax = max(amax, amax_bits8(v[ch]));
-                    if ((lane & 1) == 0) stage_code<LAYOUT>(stage, q, col / 16, a.sf_cols, code);
-                } else if ((lane & 1) == 0 && col / 16 < a.sf_stride) {
-                    stage_code<LAYOUT>(stage, q, col / 16, a.sf_cols, 0);
+                    amax = max(amax, amax_bits8(cur[k]));
+                    if ((lane & 1) == 0) {
+                        const int c = col / 16;
+                        if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+                            stage[(c >> 2) * 128 + i * 16 + q * 4 + (c & 3)] = (uint8_t)code;
+                        else
+                            stage[j * a.sf_cols + c] = (uint8_t)code;
+                    }
                 }
             }
             amax = wave_max(amax);
-            if (a.row_amax && lane == 0) a.row_amax[r0 + r] = __uint_as_float(amax << 16);
-        } else if (LAYOUT == MXQ_SF_SWIZZLED) {
-            for (int c = lane; c < a.sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, a.sf_cols, 0);
+            if (lane == 0) atomicMax(&row_max[j], amax);
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) cur[k] = nxt[k];
         }
         __syncthreads();
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-            flush_split_swz(stage, a.scales + (int64_t)a.unit_off[s] * 4 * a.sf_stride, lu,
-                            a.sf_stride);
-        else
-            flush_rows4<LAYOUT>(stage, a.scales + r0 * a.sf_cols, lu, m, a.sf_cols, a.sf_stride);
+        if (a.row_amax && (int)threadIdx.x < n_live) {
+            int q, i;
+            const int r = locate(threadIdx.x, q, i);
+            a.row_amax[e0 + r] = __uint_as_float(row_max[threadIdx.x] << 16);
+        }
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            const int tiles = a.sf_stride >> 2;
+            uint8_t *base = a.scales + (int64_t)(a.unit_off[s] >> 2) * tiles * 512 +
+                            (int64_t)band * tiles * 512 + h * 128;
+            for (int k = threadIdx.x; k < tiles * 8; k += kSplitThreads) {
+                const int t = k >> 3, part = k & 7;
+                *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512 + part * 16) =
+                    *reinterpret_cast<const u32x4 *>(stage + t * 128 + part * 16);
+            }
+        } else {
+            uint8_t *dst = a.scales + (e0 + lu * 32) * a.sf_cols;
+            const int nbytes = n_live * a.sf_cols;
+            if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                for (int k = threadIdx.x; k < (nbytes >> 4); k += kSplitThreads)
+                    *reinterpret_cast<u32x4 *>(dst + k * 16) =
+                        *reinterpret_cast<const u32x4 *>(stage + k * 16);
+                for (int k = (nbytes & ~15) + threadIdx.x; k < nbytes; k += kSplitThreads)
+                    dst[k] = stage[k];
+            } else {
+                for (int k = threadIdx.x; k < nbytes; k += kSplitThreads) dst[k] = stage[k];
+            }
+        }
         __syncthreads();
     }
 }
 
-// Fused residual add + RMSNorm + quantize, one row per wave.  The row's bf16
-// residual sum stays in registers; the sum of squares is reduced across the
-// wave in a fixed order; norm_out and the quantized form come from the same
-// bf16 values.
-template <int FMT, int LAYOUT, int NCH>
-__global__ __launch_bounds__(kThreads) void k_fused(const FusedArgs a) {
+// Fused residual add + RMSNorm + quantize.  The row's bf16 residual sum stays
+// in registers; the sum of squares is each wave's fixed-order partial,
+// combined lower half + upper half; norm_out and the quantized form come
+// from the same bf16 values.
+template <int FMT, int LAYOUT, int NCH2>
+__global__ __launch_bounds__(kRowThreads) void k_fused(const FusedArgs a) {
     using Tr = FmtTraits<FMT>;
     extern __shared__ __align__(16) uint8_t stage[];
+    __shared__ float red[8];
+    __shared__ float mult[kNvCodes];
     const int lane = threadIdx.x & (kWave - 1);
-    const int q = threadIdx.x >> 6;
+    const int w = threadIdx.x >> 6;
+    const int q = w >> 1, half = w & 1;
     const int H = a.H;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
     const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
+    if constexpr (FMT == MXQ_NVFP4) nv_fill_mult(mult, g);  // read after the first barrier
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     for (int lu = blockIdx.x; lu < a.total_units; lu += gridDim.x) {
-        const int r = wave_row<LAYOUT>(lu, q);
-        if (r < a.T) {
-            const int64_t rb = (int64_t)r * H;
-            u32x4 xv[NCH], rv[NCH];
+        const int r = LAYOUT == MXQ_SF_SWIZZLED ? (lu >> 5) * 128 + 32 * q + (lu & 31)
+                                                : lu * 4 + q;
+        const bool live = r < a.T;
+        const int64_t rb = (int64_t)r * H;
+        u32x4 xv[NCH2];
+        float acc = 0.0f;
+        if (live) {
+            u32x4 rv[NCH2];
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                const int col = ch * kChunk + lane * 8;
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
                 if (col < H) {
-                    xv[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + rb + col));
-                    rv[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.res + rb + col));
+                    xv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + rb + col));
+                    rv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.res + rb + col));
                 }
             }
-            float acc = 0.0f;
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                const int col = ch * kChunk + lane * 8;
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
                 if (col < H) {
                     u32x4 sum;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const uint32_t blo = f32_to_bf16(bf16_lo(xv[ch][j]) + bf16_lo(rv[ch][j]));
-                        const uint32_t bhi = f32_to_bf16(bf16_hi(xv[ch][j]) + bf16_hi(rv[ch][j]));
+                        const uint32_t blo = f32_to_bf16(bf16_lo(xv[k][j]) + bf16_lo(rv[k][j]));
+                        const uint32_t bhi = f32_to_bf16(bf16_hi(xv[k][j]) + bf16_hi(rv[k][j]));
                         const float flo = __uint_as_float(blo << 16);
                         const float fhi = __uint_as_float(bhi << 16);
                         acc = __builtin_fmaf(flo, flo, acc);
                         acc = __builtin_fmaf(fhi, fhi, acc);
                         sum[j] = blo | (bhi << 16);
                     }
-                    xv[ch] = sum;  // the bf16 residual sum
-                    *reinterpret_cast<u32x4 *>(a.res_out + rb + col) = sum;
+                    xv[k] = sum;  // the bf16 residual sum
+                    __builtin_nontemporal_store(sum, reinterpret_cast<u32x4 *>(a.res_out + rb + col));
                 }
             }
-            const float inv = 1.0f / __builtin_sqrtf(wave_sum(acc) / (float)H + a.eps);
-            u32x4 gm[NCH];
+            acc = wave_sum(acc);
+        }
+        if (lane == 0) red[w] = acc;
+        __syncthreads();
+        if (live) {
+            const float inv = 1.0f / __builtin_sqrtf((red[2 * q] + red[2 * q + 1]) / (float)H + a.eps);
+            u32x4 gm[NCH2];
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                const int col = ch * kChunk + lane * 8;
-                if (col < H) gm[ch] = *reinterpret_cast<const u32x4 *>(a.gamma + col);
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
+                if (col < H) gm[k] = *reinterpret_cast<const u32x4 *>(a.gamma + col);
             }
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                const int col = ch * kChunk + lane * 8;
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
                 if (col < H) {
                     u32x4 nv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float nlo = (bf16_lo(xv[ch][j]) * bf16_lo(gm[ch][j])) * inv;
-                        const float nhi = (bf16_hi(xv[ch][j]) * bf16_hi(gm[ch][j])) * inv;
+                        const float nlo = (bf16_lo(xv[k][j]) * bf16_lo(gm[k][j])) * inv;
+                        const float nhi = (bf16_hi(xv[k][j]) * bf16_hi(gm[k][j])) * inv;
                         nv[j] = pack_bf16(nlo, nhi);
                     }
-                    *reinterpret_cast<u32x4 *>(a.norm_out + rb + col) = nv;
+                    __builtin_nontemporal_store(nv, reinterpret_cast<u32x4 *>(a.norm_out + rb + col));
                     u32x2 pay;
-                    const uint32_t code = quant8<FMT>(nv, g, pay);
+                    const uint32_t code = quant8<FMT>(nv, g, mult, pay);
                     store_payload<FMT>(a.payload + (int64_t)r * payload_ld, col, pay);
                     if (leader) stage_code<LAYOUT>(stage, q, col / Tr::kBlock, a.sf_cols, code);
                 }
             }
-        } else if (LAYOUT == MXQ_SF_SWIZZLED) {
-            for (int c = lane; c < a.sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, a.sf_cols, 0);
+        } else if (LAYOUT == MXQ_SF_SWIZZLED && half == 0) {
+            stage_zero_row<LAYOUT>(stage, q, lane, a.sf_cols, a.sf_stride);
         }
         __syncthreads();
-        flush_rows4<LAYOUT>(stage, a.scales, lu, a.T, a.sf_cols, a.sf_stride);
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+            flush_interleaved_swz(stage, a.scales, lu, a.sf_stride);
+        else
+            copy_out_rows(a.scales + (int64_t)lu * 4 * a.sf_cols, stage,
+                          min(4, a.T - lu * 4) * a.sf_cols);
         __syncthreads();
     }
 }
@@ -435,32 +502,33 @@ hipError_t launch_grouped(int fmt, int layout, const GroupArgs &a, int64_t grid,
     return hipGetLastError();
 }
 
-// Row-per-wave kernels keep the whole row in registers: NCH 512-column steps.
-int row_steps(int64_t cols) {
-    const int64_t n = (cols + kChunk - 1) / kChunk;
+// Whole-row kernels keep half a row per wave in registers: NCH2 512-column
+// steps per wave.
+int half_row_steps(int64_t cols) {
+    const int64_t n = ((cols + kChunk - 1) / kChunk + 1) / 2;
+    if (n <= 1) return 1;
     if (n <= 2) return 2;
     if (n <= 4) return 4;
+    if (n <= 7) return 7;
     if (n <= 8) return 8;
-    if (n <= 14) return 14;
-    if (n <= 16) return 16;
-    return 32;
+    return 16;
 }
 
 template <int LAYOUT>
 static void split_nch(const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
-    const dim3 bd(kThreads);
-    switch (row_steps(a.cols)) {
+    const dim3 bd(kSplitThreads);
+    switch (half_row_steps(a.cols)) {
+    case 1: hipLaunchKernelGGL((k_split<LAYOUT, 1>), gd, bd, lds, s, a); break;
     case 2: hipLaunchKernelGGL((k_split<LAYOUT, 2>), gd, bd, lds, s, a); break;
     case 4: hipLaunchKernelGGL((k_split<LAYOUT, 4>), gd, bd, lds, s, a); break;
+    case 7: hipLaunchKernelGGL((k_split<LAYOUT, 7>), gd, bd, lds, s, a); break;
     case 8: hipLaunchKernelGGL((k_split<LAYOUT, 8>), gd, bd, lds, s, a); break;
-    case 14: hipLaunchKernelGGL((k_split<LAYOUT, 14>), gd, bd, lds, s, a); break;
-    case 16: hipLaunchKernelGGL((k_split<LAYOUT, 16>), gd, bd, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_split<LAYOUT, 32>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_split<LAYOUT, 16>), gd, bd, lds, s, a); break;
     }
 }
 
 hipError_t launch_split(int layout, const SplitArgs &a, int64_t grid, hipStream_t s) {
-    const size_t lds = (size_t)4 * a.sf_stride;
+    const size_t lds = (size_t)32 * a.sf_stride;
     const dim3 gd(grid_of(grid));
     if (layout == MXQ_SF_LINEAR)
         split_nch<MXQ_SF_LINEAR>(a, gd, lds, s);
@@ -471,14 +539,14 @@ hipError_t launch_split(int layout, const SplitArgs &a, int64_t grid, hipStream_
 
 template <int FMT, int LAYOUT>
 static void fused_nch(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
-    const dim3 bd(kThreads);
-    switch (row_steps(a.H)) {
+    const dim3 bd(kRowThreads);
+    switch (half_row_steps(a.H)) {
+    case 1: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 1>), gd, bd, lds, s, a); break;
     case 2: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 2>), gd, bd, lds, s, a); break;
     case 4: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 4>), gd, bd, lds, s, a); break;
+    case 7: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 7>), gd, bd, lds, s, a); break;
     case 8: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 8>), gd, bd, lds, s, a); break;
-    case 14: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 14>), gd, bd, lds, s, a); break;
-    case 16: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16>), gd, bd, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 32>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16>), gd, bd, lds, s, a); break;
     }
 }
 
