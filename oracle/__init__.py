@@ -27,6 +27,44 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 _i64 = ctypes.c_int64
 
 
+def _load(path):
+    L = ctypes.CDLL(path)
+    sig = {
+        "orc_bf16_value": (ctypes.c_double, [ctypes.c_uint16]),
+        "orc_bf16_round": (ctypes.c_uint16, [ctypes.c_double]),
+        "orc_e4m3_value": (ctypes.c_double, [ctypes.c_uint8]),
+        "orc_e4m3_encode": (ctypes.c_uint8, [ctypes.c_double]),
+        "orc_e2m1_value": (ctypes.c_double, [ctypes.c_uint8]),
+        "orc_e2m1_encode": (ctypes.c_uint8, [ctypes.c_double]),
+        "orc_e8m0_value": (ctypes.c_double, [ctypes.c_uint8]),
+        "orc_mxfp8_scale_code": (ctypes.c_uint8, [ctypes.c_double]),
+        "orc_mxfp8_multiplier": (ctypes.c_double, [ctypes.c_uint8]),
+        "orc_mxfp8_block": (None, [_u16p, ctypes.c_int, _u8p, _u8p]),
+        "orc_nvfp4_block": (None, [_u16p, ctypes.c_int, ctypes.c_float, _u8p, _u8p]),
+        "orc_sf_cols": (_i64, [_i64, ctypes.c_int]),
+        "orc_sf_bytes": (_i64, [_i64, _i64, ctypes.c_int]),
+        "orc_sf_offset": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
+        "orc_quantize": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _u16p, _i64, _i64, _i64,
+                                        ctypes.c_float, _u8p, _u8p]),
+        "orc_split_scale_offset": (_i64, [_i64p, ctypes.c_int, ctypes.c_int, _i64,
+                                          ctypes.c_int, ctypes.c_int]),
+        "orc_nvfp4_split": (ctypes.c_int, [_u16p, _i64, _i64, _i64p, ctypes.c_int,
+                                           ctypes.c_float, ctypes.c_int, _u8p, _u8p, _f32p]),
+        "orc_add_rmsnorm": (ctypes.c_int, [_u16p, _u16p, _u16p, ctypes.c_float, _i64, _i64,
+                                           _u16p, _u16p]),
+        "orc_scale_swizzle": (ctypes.c_int, [_u8p, _i64, _i64, _u8p]),
+        "orc_e4m3_encode_f32": (None, [_f32p, _i64, _u8p]),
+        "orc_e2m1_encode_f32": (None, [_f32p, _i64, _u8p]),
+        "orc_mxfp8_scale_code_bf16": (None, [_u16p, _i64, _u8p]),
+        "orc_mxfp8_elements": (None, [_u16p, _i64, ctypes.c_uint8, _u8p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib():
     """Load (building first if needed) the oracle shared library."""
     global _lib
@@ -34,42 +72,29 @@ def lib():
         if not os.path.exists(_LIB_PATH):
             from . import build as _build
             _build.build()
-        L = ctypes.CDLL(_LIB_PATH)
-        sig = {
-            "orc_bf16_value": (ctypes.c_double, [ctypes.c_uint16]),
-            "orc_bf16_round": (ctypes.c_uint16, [ctypes.c_double]),
-            "orc_e4m3_value": (ctypes.c_double, [ctypes.c_uint8]),
-            "orc_e4m3_encode": (ctypes.c_uint8, [ctypes.c_double]),
-            "orc_e2m1_value": (ctypes.c_double, [ctypes.c_uint8]),
-            "orc_e2m1_encode": (ctypes.c_uint8, [ctypes.c_double]),
-            "orc_e8m0_value": (ctypes.c_double, [ctypes.c_uint8]),
-            "orc_mxfp8_scale_code": (ctypes.c_uint8, [ctypes.c_double]),
-            "orc_mxfp8_multiplier": (ctypes.c_double, [ctypes.c_uint8]),
-            "orc_mxfp8_block": (None, [_u16p, ctypes.c_int, _u8p, _u8p]),
-            "orc_nvfp4_block": (None, [_u16p, ctypes.c_int, ctypes.c_float, _u8p, _u8p]),
-            "orc_sf_cols": (_i64, [_i64, ctypes.c_int]),
-            "orc_sf_bytes": (_i64, [_i64, _i64, ctypes.c_int]),
-            "orc_sf_offset": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
-            "orc_quantize": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _u16p, _i64, _i64, _i64,
-                                            ctypes.c_float, _u8p, _u8p]),
-            "orc_split_scale_offset": (_i64, [_i64p, ctypes.c_int, ctypes.c_int, _i64,
-                                              ctypes.c_int, ctypes.c_int]),
-            "orc_nvfp4_split": (ctypes.c_int, [_u16p, _i64, _i64, _i64p, ctypes.c_int,
-                                               ctypes.c_float, ctypes.c_int, _u8p, _u8p, _f32p]),
-            "orc_add_rmsnorm": (ctypes.c_int, [_u16p, _u16p, _u16p, ctypes.c_float, _i64, _i64,
-                                               _u16p, _u16p]),
-            "orc_scale_swizzle": (ctypes.c_int, [_u8p, _i64, _i64, _u8p]),
-            "orc_e4m3_encode_f32": (None, [_f32p, _i64, _u8p]),
-            "orc_e2m1_encode_f32": (None, [_f32p, _i64, _u8p]),
-            "orc_mxfp8_scale_code_bf16": (None, [_u16p, _i64, _u8p]),
-            "orc_mxfp8_elements": (None, [_u16p, _i64, ctypes.c_uint8, _u8p]),
-        }
-        for name, (res, args) in sig.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = _load(_LIB_PATH)
     return _lib
+
+
+class using:
+    """Context manager: route every call of this module to another build of
+    the oracle source (the mutation tests use it to check that the pins
+    reject planted mistakes)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        lib()
+        self.saved = _lib
+        _lib = _load(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def _ptr(a, t):

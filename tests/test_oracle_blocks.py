@@ -192,8 +192,13 @@ def test_split_equals_per_expert(orc):
         assert np.array_equal(amax, x.float().abs().amax(dim=1).numpy())
 
 
-def test_add_rmsnorm_pins(orc):
+@pytest.mark.parametrize("scale", [1.0, 1e-3])
+def test_add_rmsnorm_pins(orc, scale):
+    """scale 1e-3 makes mean(r^2) comparable to eps, so where eps enters
+    matters."""
     x, res, gamma = workloads.epilogue_inputs(T=7, H=512, seed=1)
+    x = (x.float() * scale).to(torch.bfloat16)
+    res = (res.float() * scale).to(torch.bfloat16)
     eps = 1e-6
     ro, no = orc.add_rmsnorm(bf16_bits(x), bf16_bits(res), bf16_bits(gamma), eps)
     # residual: torch's bf16 add rounds the exact sum once (RNE)
