@@ -26,8 +26,10 @@
  * under an fp32 encode scale g (block scale s = fp32(fp32(amax/6) * g)
  * rounded to E4M3 with saturation; element multiplier fp32(g / s_q)), E2M1
  * elements saturating at 6, two per byte, element 2j in the low nibble of
- * byte j.  Results are bit-identical to the definitions above, whatever the
- * grouping, split or launch shape.
+ * byte j.  Every NVFP4 encode scale g must lie in [2^-100, 2^100] (a device
+ * value the library cannot check; outside it results are unspecified).
+ * Results are bit-identical to the definitions above, whatever the grouping,
+ * split or launch shape.
  *
  * Scale layouts [TRT-17452, layout commit; TRT-17453, AllReduce epilogue
  * commit].  LINEAR: byte (r, c) of an [R, C] scale matrix at r*C + c.
@@ -80,8 +82,8 @@ typedef struct {
                                  [rows, cols/2]; 16-byte aligned                 */
     void *scales;             /* device u8, mxq_scale_bytes(rows, cols, fmt,
                                  layout) bytes; 16-byte aligned if swizzled     */
-    const float *global_scale;/* device fp32 scalar: NVFP4 encode scale g
-                                 (finite, > 0, <= 2^100); ignored for MXFP8     */
+    const float *global_scale;/* device fp32 scalar: NVFP4 encode scale g in
+                                 [2^-100, 2^100]; ignored for MXFP8             */
     int64_t rows;             /* >= 0 and < 2^31; 0 writes nothing             */
     int64_t src_ld;           /* row stride in elements: >= cols, multiple of 8 */
 } mxq_entry;

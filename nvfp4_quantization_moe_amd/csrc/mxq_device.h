@@ -138,25 +138,24 @@ __device__ __forceinline__ float div6(float a) {
     return __builtin_fmaf(r, r6, q);
 }
 
-// Element multipliers for every possible block-scale code: mult[k] =
-// fp32(g / decode(k)) (IEEE division), zero when decode(k) is zero or the
-// quotient is not a normal fp32 number.  Block-scale codes are 0..126 (the
-// block scale is non-negative and saturates at 448 = code 126).  Filled by
-// threads 0..126 of a workgroup; the caller synchronizes before use.
-constexpr int kNvCodes = 127;
-__device__ __forceinline__ void nv_fill_mult(float *mult, float g) {
-    const int k = threadIdx.x;
-    if (k < kNvCodes) {
-        const float sq = e4m3_decode_pos((uint32_t)k);
-        const float m = g / sq;
-        mult[k] = (sq == 0.0f || !(m >= 0x1p-126f)) ? 0.0f : m;
-    }
+// Element multiplier m = fp32(g / s_q) without a division per block.  Every
+// positive E4M3 value is s_q = d * 2^-k with d in 1..15 (d = 8 + mantissa for
+// exponent field e >= 1, k = 10 - e; d = mantissa, k = 9 for subnormals), and
+// rounding commutes with scaling by 2^k while the values stay normal, so
+// fp32(g / s_q) = fp32(g / d) * 2^k exactly.  The contract g in [2^-100,
+// 2^100] keeps g / d and g / s_q normal (so the flush of a non-normal
+// multiplier never applies).  Each wave computes the 15 quotients once, lane
+// d holding fp32(g / d) (IEEE division); a block fetches its quotient with a
+// cross-lane read, so every lane of the wave must take part in nv_scale.
+__device__ __forceinline__ float nv_wave_quot(float g) {
+    const int d = threadIdx.x & 15;
+    return g / (float)(d == 0 ? 1 : d);
 }
 
-// s = fp32(fp32(amax / 6) * g); code = E4M3(s), saturating at 448.  The
-// element multiplier comes from the table above when one is given (mult !=
-// nullptr), else from the same IEEE division done in place.
-__device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g, const float *mult) {
+// s = fp32(fp32(amax / 6) * g); code = E4M3(s), saturating at 448; multiplier
+// as above (0 for code 0, where s_q = 0).  All lanes of the wave must be
+// active.
+__device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g, float quot) {
     const float s = div6(__uint_as_float(amax_bits << 16)) * g;
     Nv4Scale r;
     // v_cvt_scalef32_pk_fp8_f32 (scale 1.0) rounds to nearest even and keeps
@@ -164,13 +163,11 @@ __device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g, const 
     const v2s k = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, __builtin_fminf(s, 448.0f),
                                                            0.0f, 1.0f, false);
     r.code = __builtin_bit_cast(uint32_t, k) & 0xFFu;
-    if (mult) {
-        r.mult = mult[r.code];
-    } else {
-        const float sq = e4m3_decode_pos(r.code);
-        const float m = g / sq;
-        r.mult = (sq == 0.0f || !(m >= 0x1p-126f)) ? 0.0f : m;
-    }
+    const uint32_t e = r.code >> 3, mant = r.code & 7u;
+    const int d = e == 0 ? (int)mant : (int)(8 + mant);
+    const int sh = e == 0 ? 9 : 10 - (int)e;
+    const float qd = __shfl(quot, d, 16);
+    r.mult = r.code == 0 ? 0.0f : __builtin_ldexpf(qd, sh);
     return r;
 }
 

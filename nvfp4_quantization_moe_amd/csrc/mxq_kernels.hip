@@ -47,14 +47,14 @@ struct FmtTraits<MXQ_NVFP4> {
     static constexpr int kLanesPerBlock = 2;
 };
 
-// Quantize one lane's 8 elements; the lanes of a block cooperate through DPP
-// (all lanes of a block must be active).  NVFP4 reads its element multiplier
-// from the workgroup's table (nv_fill_mult) or, with mult == nullptr,
-// divides in place (same quotient).  Returns the block's scale byte
-// (every lane of the block holds it) and the lane's payload: 8 bytes (MXFP8)
-// or 4 bytes in pay.x (NVFP4).
+// Quantize one lane's 8 elements; the lanes of a block cooperate through DPP,
+// and NVFP4 fetches its multiplier quotient across the wave (nv_wave_quot),
+// so every lane of the wave must call it (lanes past the tensor pass zeros
+// and discard the result).  Returns the block's scale byte (every lane of the
+// block holds it) and the lane's payload: 8 bytes (MXFP8) or 4 bytes in pay.x
+// (NVFP4).
 template <int FMT>
-__device__ __forceinline__ uint32_t quant8(u32x4 v, float g, const float *mult, u32x2 &pay) {
+__device__ __forceinline__ uint32_t quant8(u32x4 v, float g, float quot, u32x2 &pay) {
     uint32_t a = amax_bits8(v);
     if constexpr (FMT == MXQ_MXFP8) {
         a = block_max4(a);
@@ -63,7 +63,7 @@ __device__ __forceinline__ uint32_t quant8(u32x4 v, float g, const float *mult, 
         return c;
     } else {
         a = block_max2(a);
-        const Nv4Scale s = nv_scale(a, g, mult);
+        const Nv4Scale s = nv_scale(a, g, quot);
         pay.x = nv_encode8(v, s.mult);
         pay.y = 0;
         return s.code;
@@ -115,11 +115,13 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
         const int col = cc * kChunk + lane * 8;
         const bool live_col = col < a.cols;
         const float g = FMT == MXQ_NVFP4 ? *E.g : 0.0f;
+        const float quot = FMT == MXQ_NVFP4 ? nv_wave_quot(g) : 0.0f;
 
         u32x4 v[kRowsPerWave];
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
             const int r = group_row<LAYOUT>(rg, q, i);
+            v[i] = u32x4{0, 0, 0, 0};
             if (r < E.rows && live_col)
                 v[i] = __builtin_nontemporal_load(
                     reinterpret_cast<const u32x4 *>(E.src + (int64_t)r * E.ld + col));
@@ -128,10 +130,13 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
         for (int i = 0; i < kRowsPerWave; ++i) {
             const int r = group_row<LAYOUT>(rg, q, i);
             uint32_t code = 0;  // rows and columns past the tensor stage zeros
-            if (r < E.rows && live_col) {
+            if (r < E.rows) {  // uniform: the whole wave quantizes
                 u32x2 pay;
-                code = quant8<FMT>(v[i], g, nullptr, pay);  // one unit: divide in place
-                store_payload<FMT>(E.payload + (int64_t)r * payload_ld, col, pay);
+                const uint32_t c = quant8<FMT>(v[i], g, quot, pay);
+                if (live_col) {
+                    code = c;
+                    store_payload<FMT>(E.payload + (int64_t)r * payload_ld, col, pay);
+                }
             }
             if (leader) {
                 if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
@@ -236,14 +241,13 @@ template <int LAYOUT, int NCH2>
 __global__ __launch_bounds__(kSplitThreads) void k_split(const SplitArgs a) {
     extern __shared__ __align__(16) uint8_t stage[];
     __shared__ uint32_t row_max[32];
-    __shared__ float mult[kNvCodes];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int pair = w >> 1, half = w & 1;
     const int64_t payload_ld = a.cols / 2;
     const float g = *a.g;
+    const float quot = nv_wave_quot(g);
     const int stage_bytes = 32 * a.sf_stride;
-    nv_fill_mult(mult, g);  // read after the first barrier below
     for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
         int lo = 0, hi = a.n;  // split s with unit_off[s] <= u < unit_off[s + 1]
         while (hi - lo > 1) {
@@ -288,6 +292,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(const SplitArgs a) {
 #pragma unroll
             for (int k = 0; k < NCH2; ++k) {
                 const int col = (2 * k + half) * kChunk + lane * 8;
+                v[k] = u32x4{0, 0, 0, 0};
                 if (col < a.cols)
                     v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + col));
             }
@@ -309,9 +314,9 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(const SplitArgs a) {
 #pragma unroll
             for (int k = 0; k < NCH2; ++k) {
                 const int col = (2 * k + half) * kChunk + lane * 8;
+                u32x2 pay;
+                const uint32_t code = quant8<MXQ_NVFP4>(cur[k], g, quot, pay);  // whole wave
                 if (col < a.cols) {
-                    u32x2 pay;
-                    const uint32_t code = quant8<MXQ_NVFP4>(cur[k], g, mult, pay);
                     store_payload<MXQ_NVFP4>(pay_row, col, pay);
                     amax = max(amax, amax_bits8(cur[k]));
                     if ((lane & 1) == 0) {
@@ -369,14 +374,13 @@ __global__ __launch_bounds__(kRowThreads) void k_fused(const FusedArgs a) {
     using Tr = FmtTraits<FMT>;
     extern __shared__ __align__(16) uint8_t stage[];
     __shared__ float red[8];
-    __shared__ float mult[kNvCodes];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int q = w >> 1, half = w & 1;
     const int H = a.H;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
     const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
-    if constexpr (FMT == MXQ_NVFP4) nv_fill_mult(mult, g);  // read after the first barrier
+    const float quot = FMT == MXQ_NVFP4 ? nv_wave_quot(g) : 0.0f;
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     for (int lu = blockIdx.x; lu < a.total_units; lu += gridDim.x) {
         const int r = LAYOUT == MXQ_SF_SWIZZLED ? (lu >> 5) * 128 + 32 * q + (lu & 31)
@@ -429,8 +433,8 @@ __global__ __launch_bounds__(kRowThreads) void k_fused(const FusedArgs a) {
 #pragma unroll
             for (int k = 0; k < NCH2; ++k) {
                 const int col = (2 * k + half) * kChunk + lane * 8;
+                u32x4 nv = u32x4{0, 0, 0, 0};
                 if (col < H) {
-                    u32x4 nv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float nlo = (bf16_lo(xv[k][j]) * bf16_lo(gm[k][j])) * inv;
@@ -438,8 +442,10 @@ __global__ __launch_bounds__(kRowThreads) void k_fused(const FusedArgs a) {
                         nv[j] = pack_bf16(nlo, nhi);
                     }
                     __builtin_nontemporal_store(nv, reinterpret_cast<u32x4 *>(a.norm_out + rb + col));
-                    u32x2 pay;
-                    const uint32_t code = quant8<FMT>(nv, g, mult, pay);
+                }
+                u32x2 pay;
+                const uint32_t code = quant8<FMT>(nv, g, quot, pay);  // whole wave
+                if (col < H) {
                     store_payload<FMT>(a.payload + (int64_t)r * payload_ld, col, pay);
                     if (leader) stage_code<LAYOUT>(stage, q, col / Tr::kBlock, a.sf_cols, code);
                 }
