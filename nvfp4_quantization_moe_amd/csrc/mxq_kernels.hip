@@ -237,8 +237,11 @@ __device__ __forceinline__ void flush_interleaved_swz(const uint8_t *stage, uint
 // holding half of a row (512-column steps 2k + half) in registers, so short
 // experts keep every wave busy.  The row amax is the max over the two halves,
 // folded in LDS; no global atomics.
+// At most 128 VGPRs, so two workgroups share a CU (short experts give each
+// workgroup little work).
 template <int LAYOUT, int NCH2>
-__global__ __launch_bounds__(kSplitThreads) void k_split(const SplitArgs a) {
+__global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void k_split(const SplitArgs a) {
     extern __shared__ __align__(16) uint8_t stage[];
     __shared__ uint32_t row_max[32];
     const int lane = threadIdx.x & (kWave - 1);
