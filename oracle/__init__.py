@@ -50,6 +50,10 @@ def _load(path):
                                           ctypes.c_int, ctypes.c_int]),
         "orc_nvfp4_split": (ctypes.c_int, [_u16p, _i64, _i64, _i64p, ctypes.c_int,
                                            ctypes.c_float, ctypes.c_int, _u8p, _u8p, _f32p]),
+        "orc_split": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _u16p, _i64, _i64, _i64p,
+                                     ctypes.c_int, ctypes.c_float, ctypes.c_int, _u8p, _u8p,
+                                     _f32p]),
+        "orc_nvfp4_row_encode_scale": (ctypes.c_float, [ctypes.c_float]),
         "orc_add_rmsnorm": (ctypes.c_int, [_u16p, _u16p, _u16p, ctypes.c_float, _i64, _i64,
                                            _u16p, _u16p]),
         "orc_scale_swizzle": (ctypes.c_int, [_u8p, _i64, _i64, _u8p]),
@@ -205,6 +209,31 @@ def nvfp4_split(src_bits, split_rows, g, layout):
     if rc != 0:
         raise ValueError("oracle split: invalid arguments")
     return payload, scales, amax
+
+
+def split(fmt, src_bits, split_rows, g=1.0, layout=LINEAR, row_scaled=False):
+    """Split quantization in any mode: MXFP8 (g ignored), NVFP4 under one
+    encode scale g, or row-scaled NVFP4 (each row under
+    nvfp4_row_encode_scale of its own amax).
+
+    Returns (payload [T, cols or cols/2], bulk scales, row_amax fp32 [T])."""
+    src = np.ascontiguousarray(src_bits, dtype=np.uint16)
+    T, cols = src.shape
+    sr = np.ascontiguousarray(split_rows, dtype=np.int64)
+    total_sf = split_scale_offset(sr, len(sr), cols, fmt, layout)
+    payload = np.zeros((T, cols if fmt == MXFP8 else cols // 2), np.uint8)
+    scales = np.zeros(total_sf, np.uint8)
+    amax = np.zeros(T, np.float32)
+    rc = lib().orc_split(fmt, int(bool(row_scaled)), _ptr(src, _u16p), T, cols, _ptr(sr, _i64p),
+                         len(sr), float(g), layout, _ptr(payload, _u8p), _ptr(scales, _u8p),
+                         _ptr(amax, _f32p))
+    if rc != 0:
+        raise ValueError("oracle split: invalid arguments")
+    return payload, scales, amax
+
+
+def nvfp4_row_encode_scale(amax):
+    return lib().orc_nvfp4_row_encode_scale(float(amax))
 
 
 def add_rmsnorm(x_bits, res_bits, gamma_bits, eps):

@@ -338,36 +338,96 @@ int64_t orc_split_scale_offset(const int64_t *split_rows, int n, int i, int64_t 
     return off;
 }
 
-int orc_nvfp4_split(const uint16_t *src, int64_t total_rows, int64_t cols, const int64_t *split_rows,
-                    int n, float g, int layout, uint8_t *payload, uint8_t *scales, float *row_amax)
+/* Row-scaled NVFP4 [TE-3800, Description: the activation's second-level
+ * scale is per row and derived from that row's amax].  The pages do not print
+ * the formula; the per-tensor convention (an encode scale that maps the amax
+ * onto the largest E4M3 block scale 448 times the largest E2M1 element 6)
+ * applied to one row gives g_r = fp32(2688 / a), a correctly rounded fp32
+ * division.  An all-zero row takes g_r = 1 (any value quantizes it to zeros),
+ * and g_r is clamped to [2^-100, 2^100], the range in which every block
+ * multiplier g_r / s_q stays a finite normal fp32 number; rows reach the
+ * clamp only when a < 2688 * 2^-100 or a > 2688 * 2^100. */
+float orc_nvfp4_row_encode_scale(float amax)
 {
-    int64_t o = 0, sum = 0, r, j;
+    float g, lo = (float)ldexp(1.0, -100), hi = (float)ldexp(1.0, 100);
+    assert(amax >= 0.0f && isfinite(amax));
+    if (amax == 0.0f)
+        return 1.0f;
+    g = 2688.0f / amax; /* fp32 division, correctly rounded (may overflow to inf) */
+    if (g < lo)
+        g = lo;
+    if (g > hi)
+        g = hi;
+    return g;
+}
+
+static float row_amax_of(const uint16_t *x, int64_t cols)
+{
+    double amax = 0.0;
+    int64_t j;
+    for (j = 0; j < cols; ++j) {
+        double v = fabs(orc_bf16_value(x[j]));
+        assert(isfinite(v));
+        if (v > amax)
+            amax = v;
+    }
+    return (float)amax; /* exact: a bf16 value */
+}
+
+int orc_split(int fmt, int row_scaled, const uint16_t *src, int64_t total_rows, int64_t cols,
+              const int64_t *split_rows, int n, float g, int layout, uint8_t *payload,
+              uint8_t *scales, float *row_amax)
+{
+    int64_t o = 0, sum = 0, bs = fmt == ORC_MXFP8 ? 32 : 16, r;
+    int64_t payload_row = fmt == ORC_MXFP8 ? cols : cols / 2;
+    int64_t C;
     int i;
+    if ((fmt != ORC_MXFP8 && fmt != ORC_NVFP4) || (row_scaled && fmt != ORC_NVFP4))
+        return -1;
+    if (layout != ORC_LINEAR && layout != ORC_SWIZZLED)
+        return -1;
     for (i = 0; i < n; ++i) {
         if (split_rows[i] < 0)
             return -1;
         sum += split_rows[i];
     }
-    if (sum != total_rows || cols <= 0 || cols % 16 != 0)
+    if (sum != total_rows || cols <= 0 || cols % bs != 0)
         return -1;
+    C = orc_sf_cols(cols, fmt);
     for (i = 0; i < n; ++i) {
         int64_t m = split_rows[i];
-        int64_t base = orc_split_scale_offset(split_rows, n, i, cols, ORC_NVFP4, layout);
-        if (m > 0 && orc_quantize(ORC_NVFP4, layout, src + o * cols, m, cols, cols, g,
-                                  payload + o * (cols / 2), scales + base) != 0)
-            return -1;
+        int64_t base = orc_split_scale_offset(split_rows, n, i, cols, fmt, layout);
+        if (m > 0 && !row_scaled) {
+            /* the expert's rows form one tensor with its own scale matrix */
+            if (orc_quantize(fmt, layout, src + o * cols, m, cols, cols, g,
+                             payload + o * payload_row, scales + base) != 0)
+                return -1;
+        } else if (m > 0) {
+            /* each row under its own encode scale; local row index r - o */
+            memset(scales + base, 0, (size_t)orc_sf_bytes(m, C, layout));
+            for (r = 0; r < m; ++r) {
+                const uint16_t *x = src + (o + r) * cols;
+                float gr = orc_nvfp4_row_encode_scale(row_amax_of(x, cols));
+                int64_t c;
+                for (c = 0; c < C; ++c) {
+                    uint8_t sc;
+                    orc_nvfp4_block(x + c * 16, 16, gr, payload + (o + r) * payload_row + c * 8, &sc);
+                    scales[base + orc_sf_offset(r, c, C, layout)] = sc;
+                }
+            }
+        }
         o += m;
     }
-    for (r = 0; r < total_rows; ++r) {
-        double amax = 0.0;
-        for (j = 0; j < cols; ++j) {
-            double v = fabs(orc_bf16_value(src[r * cols + j]));
-            if (v > amax)
-                amax = v;
-        }
-        row_amax[r] = (float)amax; /* exact */
-    }
+    for (r = 0; r < total_rows; ++r)
+        row_amax[r] = row_amax_of(src + r * cols, cols);
     return 0;
+}
+
+int orc_nvfp4_split(const uint16_t *src, int64_t total_rows, int64_t cols, const int64_t *split_rows,
+                    int n, float g, int layout, uint8_t *payload, uint8_t *scales, float *row_amax)
+{
+    return orc_split(ORC_NVFP4, 0, src, total_rows, cols, split_rows, n, g, layout, payload,
+                     scales, row_amax);
 }
 
 /* Residual add + RMSNorm [TRT-17452, fold commit; TRT-17453, AllReduce

@@ -76,3 +76,26 @@ def e4m3_table() -> np.ndarray:
     """All 256 E4M3 code values via torch's float8_e4m3fn decode (float64)."""
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
     return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def row_scaled_rows():
+    """Parse tests/golden/row_scaled_rows.txt -> list of dicts (32-element rows)."""
+    cases = []
+    with open(os.path.join(GOLDEN, "row_scaled_rows.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            d = {"id": parts[0]}
+            for p in parts[1:]:
+                k, v = p.split("=")
+                if k == "g":
+                    d[k] = float.fromhex(v)
+                elif k == "amax":
+                    d[k] = int(v, 16)
+                else:
+                    d[k] = _expand(v)
+            assert len(d["x"]) == 32 and len(d["payload"]) == 16 and len(d["scales"]) == 2, d["id"]
+            cases.append(d)
+    return cases

@@ -17,7 +17,8 @@ sys.path.insert(0, os.path.dirname(HERE))
 import oracle  # noqa: E402
 import test_oracle_blocks as B  # noqa: E402
 import test_oracle_formats as F  # noqa: E402
-from helpers import hand_blocks  # noqa: E402
+import test_oracle_split_modes as S  # noqa: E402
+from helpers import hand_blocks, row_scaled_rows  # noqa: E402
 
 
 def checks():
@@ -40,6 +41,13 @@ def checks():
     yield "layouts", lambda o: [B.test_quantize_rows_independent_and_layouts_agree(o, f)
                                 for f in (0, 1)]
     yield "split", B.test_split_equals_per_expert
+    yield "row_hand", lambda o: [S.test_row_scaled_hand_row(o, c) for c in row_scaled_rows()]
+    yield "row_scale_values", S.test_row_encode_scale_special_values
+    yield "row_equal_amax", S.test_row_scaled_equal_amax_reduces_to_tensor_scaled
+    yield "row_max_six", S.test_row_scaled_row_max_encodes_as_six
+    yield "row_split_indep", S.test_row_scaled_rows_independent_of_split
+    yield "mx_split_sizes", S.test_mxfp8_split_sizes_by_hand
+    yield "mx_split", S.test_mxfp8_split_equals_per_expert
     yield "rmsnorm", lambda o: [B.test_add_rmsnorm_pins(o, sc) for sc in (1.0, 1e-3)]
 
 

@@ -48,6 +48,17 @@ MUTANTS = [
     ("residual_not_rounded",
      "uint16_t rb = orc_bf16_round(orc_bf16_value(x[t * H + j]) + orc_bf16_value(res[t * H + j]));",
      "uint16_t rb = orc_bf16_round(orc_bf16_value(x[t * H + j]));"),
+    ("row_scale_unclamped", "    if (g > hi)\n        g = hi;\n", ""),
+    ("row_scale_clamped_at_flt_max", "    if (g > hi)\n        g = hi;\n",
+     "    if (g > FLT_MAX)\n        g = FLT_MAX;\n"),
+    ("row_scale_zero_row_unity_dropped", "    if (amax == 0.0f)\n        return 1.0f;\n", ""),
+    ("row_scale_without_e2m1_max", "g = 2688.0f / amax;", "g = 448.0f / amax;"),
+    ("row_scaled_local_row_ignored",
+     "scales[base + orc_sf_offset(r, c, C, layout)] = sc;",
+     "scales[base + orc_sf_offset(r ? r - 1 : 0, c, C, layout)] = sc;"),
+    ("split_payload_row_width_nvfp4",
+     "int64_t payload_row = fmt == ORC_MXFP8 ? cols : cols / 2;\n    int64_t C;",
+     "int64_t payload_row = cols / 2;\n    int64_t C;"),
 ]
 
 
