@@ -131,6 +131,41 @@ int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols,
                       void *payload, void *scales, float *row_amax, int layout, void *stream);
 
 /*
+ * nvfp4_quant_split_row_scaled -- the split of nvfp4_quant_split with a
+ * second-level scale per row instead of one per tensor [TE-3800,
+ * Description: row-scaled NVFP4 activations are quantized once and their
+ * payload and row-scale metadata partitioned per expert; diagram: split
+ * packed values and row amax].  Row r is quantized under its own encode scale
+ *     g_r = 1                                   if a_r = 0,
+ *     g_r = clamp(fp32(2688 / a_r), 2^-100, 2^100)  otherwise,
+ * a_r = max_j |src[r, j]| (2688 = 448 * 6: the row amax lands on the largest
+ * E4M3 block scale times the largest E2M1 element; the pages print no
+ * formula, this is the per-tensor convention applied per row, and the clamp
+ * keeps every block multiplier finite and normal).  The decode scale of row r
+ * is 1 / g_r, which a consumer recomputes from row_amax.
+ *   row_amax     device fp32 [total_rows], REQUIRED: a_r of every row
+ * Everything else as nvfp4_quant_split (no global_scale).
+ */
+int nvfp4_quant_split_row_scaled(const void *src, int64_t total_rows, int64_t cols,
+                                 const int64_t *split_rows, int n_splits, void *payload,
+                                 void *scales, float *row_amax, int layout, void *stream);
+
+/*
+ * mxfp8_quant_split -- the same quantize-once-and-split for MXFP8 [TE-3800,
+ * Description: MXFP8 is the control of the split measurements].
+ *   payload      device u8 [total_rows, cols]; expert i's rows [o_i, o_i + m_i)
+ *   scales       bulk buffer as in nvfp4_quant_split with fmt MXQ_MXFP8:
+ *                expert i at mxq_split_scale_offset(..., i, cols, MXQ_MXFP8,
+ *                layout), [m_i, cols/32] in `layout`, swizzled rows padded per
+ *                expert to 128
+ *   row_amax     device fp32 [total_rows] or NULL
+ * cols is a multiple of 32, at most 16384.
+ */
+int mxfp8_quant_split(const void *src, int64_t total_rows, int64_t cols,
+                      const int64_t *split_rows, int n_splits, void *payload, void *scales,
+                      float *row_amax, int layout, void *stream);
+
+/*
  * rmsnorm_quant_fused -- residual add + RMSNorm + block quantization in one
  * pass [TRT-17452, fold commit: the epilogue quantizes the same bf16 values
  * it writes to norm_out; TRT-17453, AllReduce epilogue commit: bitwise equal

@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
             "mx_quant_grouped": (ci, [ci, ci, i64, ctypes.POINTER(_Entry), ci, vp]),
             "nvfp4_quant_split": (ci, [vp, i64, i64, ctypes.POINTER(i64), ci, vp, vp, vp, vp,
                                        ci, vp]),
+            "nvfp4_quant_split_row_scaled": (ci, [vp, i64, i64, ctypes.POINTER(i64), ci, vp, vp,
+                                                  vp, ci, vp]),
+            "mxfp8_quant_split": (ci, [vp, i64, i64, ctypes.POINTER(i64), ci, vp, vp, vp, ci,
+                                       vp]),
             "rmsnorm_quant_fused": (ci, [ci, ci, vp, vp, vp, cf, i64, i64, vp, vp, vp, vp, vp,
                                          vp]),
             "scale_swizzle": (ci, [vp, i64, i64, vp, vp]),
@@ -220,24 +224,16 @@ def _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales):
     return payloads, scales
 
 
-def nvfp4_quant_split(src: torch.Tensor, split_rows: Sequence[int], global_scale: torch.Tensor,
-                      layout: int = SWIZZLED, payload: Optional[torch.Tensor] = None,
-                      scales: Optional[torch.Tensor] = None,
-                      row_amax: Optional[torch.Tensor] = None, want_row_amax: bool = True):
-    """Quantize a concatenated bf16 activation [T, H] once and split it per
-    expert.  Returns (payload [T, H/2], bulk scales, row_amax [T] or None);
-    expert i's scales start at split_scale_offset(split_rows, i, H)."""
+def _split_outputs(fmt, src, split_rows, layout, payload, scales, row_amax, want_row_amax):
     _need_gpu(src, "src", torch.bfloat16)
-    _need_gpu(global_scale, "global_scale", torch.float32)
     if src.dim() != 2 or not src.is_contiguous():
         raise ValueError("src must be a contiguous [T, H] bf16 tensor")
     T, H = src.shape
-    split_rows = [int(v) for v in split_rows]
     dev = src.device
     if payload is None:
-        payload = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+        payload = torch.empty((T, H if fmt == MXFP8 else H // 2), dtype=torch.uint8, device=dev)
     if scales is None:
-        total = split_scale_offset(split_rows, len(split_rows), H, NVFP4, layout)
+        total = split_scale_offset(split_rows, len(split_rows), H, fmt, layout)
         scales = torch.empty(total, dtype=torch.uint8, device=dev)
     if row_amax is None and want_row_amax:
         row_amax = torch.empty(T, dtype=torch.float32, device=dev)
@@ -246,10 +242,55 @@ def nvfp4_quant_split(src: torch.Tensor, split_rows: Sequence[int], global_scale
     if row_amax is not None:
         _need_gpu(row_amax, "row_amax", torch.float32)
     arr = (ctypes.c_int64 * max(len(split_rows), 1))(*split_rows)
+    return T, H, payload, scales, row_amax, arr
+
+
+def nvfp4_quant_split(src: torch.Tensor, split_rows: Sequence[int], global_scale: torch.Tensor,
+                      layout: int = SWIZZLED, payload: Optional[torch.Tensor] = None,
+                      scales: Optional[torch.Tensor] = None,
+                      row_amax: Optional[torch.Tensor] = None, want_row_amax: bool = True):
+    """Quantize a concatenated bf16 activation [T, H] once and split it per
+    expert.  Returns (payload [T, H/2], bulk scales, row_amax [T] or None);
+    expert i's scales start at split_scale_offset(split_rows, i, H)."""
+    _need_gpu(global_scale, "global_scale", torch.float32)
+    split_rows = [int(v) for v in split_rows]
+    T, H, payload, scales, row_amax, arr = _split_outputs(
+        NVFP4, src, split_rows, layout, payload, scales, row_amax, want_row_amax)
     rc = lib().nvfp4_quant_split(src.data_ptr(), T, H, arr, len(split_rows),
                                  global_scale.data_ptr(), payload.data_ptr(), scales.data_ptr(),
-                                 _ptr(row_amax), layout, _stream(dev))
+                                 _ptr(row_amax), layout, _stream(src.device))
     _check(rc, "nvfp4_quant_split")
+    return payload, scales, row_amax
+
+
+def nvfp4_quant_split_row_scaled(src: torch.Tensor, split_rows: Sequence[int],
+                                 layout: int = SWIZZLED, payload: Optional[torch.Tensor] = None,
+                                 scales: Optional[torch.Tensor] = None,
+                                 row_amax: Optional[torch.Tensor] = None):
+    """Row-scaled NVFP4 split: row r under its own encode scale from its amax.
+    Returns (payload [T, H/2], bulk scales, row_amax [T])."""
+    split_rows = [int(v) for v in split_rows]
+    T, H, payload, scales, row_amax, arr = _split_outputs(
+        NVFP4, src, split_rows, layout, payload, scales, row_amax, True)
+    rc = lib().nvfp4_quant_split_row_scaled(src.data_ptr(), T, H, arr, len(split_rows),
+                                            payload.data_ptr(), scales.data_ptr(),
+                                            row_amax.data_ptr(), layout, _stream(src.device))
+    _check(rc, "nvfp4_quant_split_row_scaled")
+    return payload, scales, row_amax
+
+
+def mxfp8_quant_split(src: torch.Tensor, split_rows: Sequence[int], layout: int = SWIZZLED,
+                      payload: Optional[torch.Tensor] = None,
+                      scales: Optional[torch.Tensor] = None,
+                      row_amax: Optional[torch.Tensor] = None, want_row_amax: bool = True):
+    """MXFP8 split.  Returns (payload [T, H], bulk scales, row_amax [T] or
+    None); expert i's scales start at split_scale_offset(split_rows, i, H, MXFP8)."""
+    split_rows = [int(v) for v in split_rows]
+    T, H, payload, scales, row_amax, arr = _split_outputs(
+        MXFP8, src, split_rows, layout, payload, scales, row_amax, want_row_amax)
+    rc = lib().mxfp8_quant_split(src.data_ptr(), T, H, arr, len(split_rows), payload.data_ptr(),
+                                 scales.data_ptr(), _ptr(row_amax), layout, _stream(src.device))
+    _check(rc, "mxfp8_quant_split")
     return payload, scales, row_amax
 
 

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmxq.so")
-SOURCES = ["mxq_kernels.hip", "mxq_api.hip"]
+SOURCES = ["mxq_grouped.hip", "mxq_split.hip", "mxq_fused.hip", "mxq_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -113,9 +113,15 @@ int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries
     return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;
 }
 
-int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols, const int64_t *split_rows,
-                      int n_splits, const float *global_scale, void *payload, void *scales,
-                      float *row_amax, int layout, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The three split forms share validation and launch packing.  row_scaled
+// implies NVFP4; g is read only for tensor-scaled NVFP4.
+int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, int64_t cols,
+                const int64_t *split_rows, int n_splits, const float *global_scale,
+                void *payload, void *scales, float *row_amax, int layout, void *stream) {
     if (!valid_layout(layout) || !split_rows || n_splits < 1 || total_rows < 0 ||
         total_rows >= (int64_t)1 << 31)
         return MXQ_EINVAL;
@@ -125,14 +131,17 @@ int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols, const i
         sum += split_rows[i];
     }
     if (sum != total_rows) return MXQ_EINVAL;
-    if (cols <= 0 || cols % 16 != 0 || cols > kMaxColsNv) return MXQ_ESHAPE;
+    if (cols <= 0 || cols % block_of(fmt) != 0 || cols > kMaxSplitCols) return MXQ_ESHAPE;
     if (total_rows == 0) return MXQ_OK;
-    if (!src || !global_scale || !payload || !scales) return MXQ_EINVAL;
+    if (!src || !payload || !scales) return MXQ_EINVAL;
+    if (fmt == MXQ_NVFP4 && !row_scaled && !global_scale) return MXQ_EINVAL;
+    if (row_scaled && !row_amax) return MXQ_EINVAL;
     if (!aligned16(src) || !aligned16(payload)) return MXQ_ESHAPE;
     if (layout == MXQ_SF_SWIZZLED && !aligned16(scales)) return MXQ_ESHAPE;
 
-    const int64_t C = cols / 16;
+    const int64_t C = cols / block_of(fmt);
     const int64_t Cs = layout == MXQ_SF_SWIZZLED ? round_up(C, 4) : C;
+    const int64_t payload_ld = fmt == MXQ_MXFP8 ? cols : cols / 2;
     int64_t row_base = 0, scale_base = 0;
     for (int first = 0; first < n_splits; first += kMaxSplitsPerLaunch) {
         const int n = n_splits - first < kMaxSplitsPerLaunch ? n_splits - first
@@ -140,7 +149,7 @@ int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols, const i
         SplitArgs a;
         memset(&a, 0, sizeof(a));
         a.src = static_cast<const uint16_t *>(src) + row_base * cols;
-        a.payload = static_cast<uint8_t *>(payload) + row_base * (cols / 2);
+        a.payload = static_cast<uint8_t *>(payload) + row_base * payload_ld;
         a.scales = static_cast<uint8_t *>(scales) + scale_base;
         a.row_amax = row_amax ? row_amax + row_base : nullptr;
         a.g = global_scale;
@@ -162,13 +171,39 @@ int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols, const i
         a.unit_off[n] = (int32_t)units;
         a.total_units = (int32_t)units;
         if (units > 0) {
-            hipError_t err = launch_split(layout, a, grid_for(units), (hipStream_t)stream);
+            hipError_t err =
+                launch_split(fmt, row_scaled, layout, a, grid_for(units), (hipStream_t)stream);
             if (err != hipSuccess) return MXQ_ELAUNCH;
         }
         row_base += rows;
         scale_base += sbytes;
     }
     return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols, const int64_t *split_rows,
+                      int n_splits, const float *global_scale, void *payload, void *scales,
+                      float *row_amax, int layout, void *stream) {
+    return quant_split(MXQ_NVFP4, false, src, total_rows, cols, split_rows, n_splits,
+                       global_scale, payload, scales, row_amax, layout, stream);
+}
+
+int nvfp4_quant_split_row_scaled(const void *src, int64_t total_rows, int64_t cols,
+                                 const int64_t *split_rows, int n_splits, void *payload,
+                                 void *scales, float *row_amax, int layout, void *stream) {
+    return quant_split(MXQ_NVFP4, true, src, total_rows, cols, split_rows, n_splits, nullptr,
+                       payload, scales, row_amax, layout, stream);
+}
+
+int mxfp8_quant_split(const void *src, int64_t total_rows, int64_t cols, const int64_t *split_rows,
+                      int n_splits, void *payload, void *scales, float *row_amax, int layout,
+                      void *stream) {
+    return quant_split(MXQ_MXFP8, false, src, total_rows, cols, split_rows, n_splits, nullptr,
+                       payload, scales, row_amax, layout, stream);
 }
 
 int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual,

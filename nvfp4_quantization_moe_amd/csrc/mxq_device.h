@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mxq.h"
+
 namespace mxq {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -185,13 +187,51 @@ __device__ __forceinline__ uint32_t nv_encode8(u32x4 v, float m) {
     return out;
 }
 
-// ---- swizzled 128x4 scale layout ----------------------------------------------
-// Work units are 32 rows.  With the swizzled layout a unit takes the rows
-// band*128 + 32*q + 8*g + i (q = wave 0..3, i = 0..7) of one 128-row band, so
-// in every 512-byte tile it fills exactly one 128-byte line (line g).  The
-// unit stages those lines in LDS: tile t's line at stage[t*128 + i*16 + q*4 + c%4].
-__device__ __forceinline__ int stage_index_swz(int q, int i, int c) {
-    return (c >> 2) * 128 + i * 16 + q * 4 + (c & 3);
+// ---- shared per-lane quantization step ----------------------------------------
+template <int FMT>
+struct FmtTraits;
+template <>
+struct FmtTraits<MXQ_MXFP8> {
+    static constexpr int kBlock = 32;
+    static constexpr int kLanesPerBlock = 4;
+};
+template <>
+struct FmtTraits<MXQ_NVFP4> {
+    static constexpr int kBlock = 16;
+    static constexpr int kLanesPerBlock = 2;
+};
+
+// Quantize one lane's 8 elements; the lanes of a block cooperate through DPP,
+// and NVFP4 fetches its multiplier quotient across the wave (nv_wave_quot),
+// so every lane of the wave must call it (lanes past the tensor pass zeros
+// and discard the result).  Returns the block's scale byte (every lane of the
+// block holds it) and the lane's payload: 8 bytes (MXFP8) or 4 bytes in pay.x
+// (NVFP4).
+template <int FMT>
+__device__ __forceinline__ uint32_t quant8(u32x4 v, float g, float quot, u32x2 &pay) {
+    uint32_t a = amax_bits8(v);
+    if constexpr (FMT == MXQ_MXFP8) {
+        a = block_max4(a);
+        const uint32_t c = mx_scale_code(a);
+        pay = mx_encode8(v, c);
+        return c;
+    } else {
+        a = block_max2(a);
+        const Nv4Scale s = nv_scale(a, g, quot);
+        pay.x = nv_encode8(v, s.mult);
+        pay.y = 0;
+        return s.code;
+    }
+}
+
+// Payload bytes are written once and not read back by this kernel: streaming
+// (non-temporal) stores keep them from displacing cache lines.
+template <int FMT>
+__device__ __forceinline__ void store_payload(uint8_t *row_payload, int col, u32x2 pay) {
+    if constexpr (FMT == MXQ_MXFP8)
+        __builtin_nontemporal_store(pay, reinterpret_cast<u32x2 *>(row_payload + col));
+    else
+        __builtin_nontemporal_store(pay.x, reinterpret_cast<uint32_t *>(row_payload + (col >> 1)));
 }
 
 }  // namespace mxq

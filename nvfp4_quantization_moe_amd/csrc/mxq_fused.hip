@@ -1,0 +1,221 @@
+// mxq_fused.hip -- the fused residual add + RMSNorm + quantize epilogue, and
+// the linear -> swizzled scale conversion.
+//
+// The epilogue needs whole rows (the RMSNorm sum of squares): two waves own
+// one row and hold it in registers; a unit is 4 rows.  Swizzled units take
+// rows band*128 + 32*q + gi (gi = 0..31), so a unit writes one 16-byte piece
+// of each tile line (8 consecutive units complete it).  Unit u runs on
+// workgroup u in plain dispatch order; every byte has one writer.
+#include "mxq_device.h"
+#include "mxq_internal.h"
+
+namespace mxq {
+
+// ---------------------------------------------------------------------------
+// Whole-row units: 4 rows per workgroup of 8 waves, two waves per row; each
+// wave holds half of its row in registers (512-column steps 2k + half).  The
+// sum of squares combines the two halves through LDS in a fixed order.
+// Staged scales: swizzled [tile][row][4] (16 bytes per tile), linear [row][C].
+// ---------------------------------------------------------------------------
+template <int LAYOUT>
+__device__ __forceinline__ void stage_code(uint8_t *stage, int q, int c, int sf_cols,
+                                           uint32_t code) {
+    if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+        stage[(c >> 2) * 16 + q * 4 + (c & 3)] = (uint8_t)code;
+    else
+        stage[q * sf_cols + c] = (uint8_t)code;
+}
+
+// Zero the staged codes of a row with no data (swizzled padding rows).
+template <int LAYOUT>
+__device__ __forceinline__ void stage_zero_row(uint8_t *stage, int q, int lane, int sf_cols,
+                                               int sf_stride) {
+    for (int c = lane; c < sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, sf_cols, 0);
+}
+
+// Copy n staged bytes to global memory with kRowThreads threads.
+__device__ __forceinline__ void copy_out_rows(uint8_t *dst, const uint8_t *src, int n) {
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        const int nv = n >> 4;
+        for (int k = threadIdx.x; k < nv; k += kRowThreads)
+            *reinterpret_cast<u32x4 *>(dst + k * 16) = *reinterpret_cast<const u32x4 *>(src + k * 16);
+        for (int k = (nv << 4) + threadIdx.x; k < n; k += kRowThreads) dst[k] = src[k];
+    } else {
+        for (int k = threadIdx.x; k < n; k += kRowThreads) dst[k] = src[k];
+    }
+}
+
+// Fused swizzled units take rows band*128 + 32*q + gi (gi = lu mod 32): one
+// 16-byte piece per tile line.
+__device__ __forceinline__ void flush_interleaved_swz(const uint8_t *stage, uint8_t *region,
+                                                      int lu, int sf_stride) {
+    const int tiles = sf_stride >> 2;
+    uint8_t *base = region + (int64_t)(lu >> 5) * tiles * 512 + (lu & 31) * 16;
+    for (int t = threadIdx.x; t < tiles; t += kRowThreads)
+        *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512) =
+            *reinterpret_cast<const u32x4 *>(stage + t * 16);
+}
+
+// Fused residual add + RMSNorm + quantize.  The row's bf16 residual sum stays
+// in registers; the sum of squares is each wave's fixed-order partial,
+// combined lower half + upper half; norm_out and the quantized form come
+// from the same bf16 values.
+template <int FMT, int LAYOUT, int NCH2>
+__global__ __launch_bounds__(kRowThreads) void k_fused(const FusedArgs a) {
+    using Tr = FmtTraits<FMT>;
+    extern __shared__ __align__(16) uint8_t stage[];
+    __shared__ float red[8];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int q = w >> 1, half = w & 1;
+    const int H = a.H;
+    const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
+    const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
+    const float quot = FMT == MXQ_NVFP4 ? nv_wave_quot(g) : 0.0f;
+    const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
+    for (int lu = blockIdx.x; lu < a.total_units; lu += gridDim.x) {
+        const int r = LAYOUT == MXQ_SF_SWIZZLED ? (lu >> 5) * 128 + 32 * q + (lu & 31)
+                                                : lu * 4 + q;
+        const bool live = r < a.T;
+        const int64_t rb = (int64_t)r * H;
+        u32x4 xv[NCH2];
+        float acc = 0.0f;
+        if (live) {
+            u32x4 rv[NCH2];
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
+                if (col < H) {
+                    xv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + rb + col));
+                    rv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.res + rb + col));
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
+                if (col < H) {
+                    u32x4 sum;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t blo = f32_to_bf16(bf16_lo(xv[k][j]) + bf16_lo(rv[k][j]));
+                        const uint32_t bhi = f32_to_bf16(bf16_hi(xv[k][j]) + bf16_hi(rv[k][j]));
+                        const float flo = __uint_as_float(blo << 16);
+                        const float fhi = __uint_as_float(bhi << 16);
+                        acc = __builtin_fmaf(flo, flo, acc);
+                        acc = __builtin_fmaf(fhi, fhi, acc);
+                        sum[j] = blo | (bhi << 16);
+                    }
+                    xv[k] = sum;  // the bf16 residual sum
+                    __builtin_nontemporal_store(sum, reinterpret_cast<u32x4 *>(a.res_out + rb + col));
+                }
+            }
+            acc = wave_sum(acc);
+        }
+        if (lane == 0) red[w] = acc;
+        __syncthreads();
+        if (live) {
+            const float inv = 1.0f / __builtin_sqrtf((red[2 * q] + red[2 * q + 1]) / (float)H + a.eps);
+            u32x4 gm[NCH2];
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
+                if (col < H) gm[k] = *reinterpret_cast<const u32x4 *>(a.gamma + col);
+            }
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
+                u32x4 nv = u32x4{0, 0, 0, 0};
+                if (col < H) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float nlo = (bf16_lo(xv[k][j]) * bf16_lo(gm[k][j])) * inv;
+                        const float nhi = (bf16_hi(xv[k][j]) * bf16_hi(gm[k][j])) * inv;
+                        nv[j] = pack_bf16(nlo, nhi);
+                    }
+                    __builtin_nontemporal_store(nv, reinterpret_cast<u32x4 *>(a.norm_out + rb + col));
+                }
+                u32x2 pay;
+                const uint32_t code = quant8<FMT>(nv, g, quot, pay);  // whole wave
+                if (col < H) {
+                    store_payload<FMT>(a.payload + (int64_t)r * payload_ld, col, pay);
+                    if (leader) stage_code<LAYOUT>(stage, q, col / Tr::kBlock, a.sf_cols, code);
+                }
+            }
+        } else if (LAYOUT == MXQ_SF_SWIZZLED && half == 0) {
+            stage_zero_row<LAYOUT>(stage, q, lane, a.sf_cols, a.sf_stride);
+        }
+        __syncthreads();
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+            flush_interleaved_swz(stage, a.scales, lu, a.sf_stride);
+        else
+            copy_out_rows(a.scales + (int64_t)lu * 4 * a.sf_cols, stage,
+                          min(4, a.T - lu * 4) * a.sf_cols);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Linear -> swizzled scale layout.  One thread per 16-byte output vector:
+// rows 32*q + i (q = 0..3) of a 128-row band, 4 columns each; padding is 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_swizzle(const SwizzleArgs a) {
+    for (int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x; k < a.n_vec;
+         k += (int64_t)gridDim.x * kThreads) {
+        const int64_t tile = k >> 5;
+        const int i = (int)(k & 31);
+        const int64_t band = tile / a.tiles_per_band;
+        const int64_t c0 = (tile % a.tiles_per_band) * 4;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t r = band * 128 + 32 * q + i;
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t c = c0 + j;
+                if (r < a.rows && c < a.cols) word |= (uint32_t)a.lin[r * a.cols + c] << (8 * j);
+            }
+            w[q] = word;
+        }
+        *reinterpret_cast<u32x4 *>(a.swz + k * 16) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+static inline unsigned grid_of(int64_t g) { return (unsigned)(g < 1 ? 1 : g); }
+
+template <int FMT, int LAYOUT>
+static void fused_nch(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
+    const dim3 bd(kRowThreads);
+    switch (half_row_steps(a.H)) {
+    case 1: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 1>), gd, bd, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 2>), gd, bd, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 4>), gd, bd, lds, s, a); break;
+    case 7: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 7>), gd, bd, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 8>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16>), gd, bd, lds, s, a); break;
+    }
+}
+
+hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s) {
+    const size_t lds = (size_t)4 * a.sf_stride;
+    const dim3 gd(grid_of(grid));
+    if (fmt == MXQ_MXFP8 && layout == MXQ_SF_LINEAR)
+        fused_nch<MXQ_MXFP8, MXQ_SF_LINEAR>(a, gd, lds, s);
+    else if (fmt == MXQ_MXFP8)
+        fused_nch<MXQ_MXFP8, MXQ_SF_SWIZZLED>(a, gd, lds, s);
+    else if (layout == MXQ_SF_LINEAR)
+        fused_nch<MXQ_NVFP4, MXQ_SF_LINEAR>(a, gd, lds, s);
+    else
+        fused_nch<MXQ_NVFP4, MXQ_SF_SWIZZLED>(a, gd, lds, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_swizzle(const SwizzleArgs &a, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL(k_swizzle, dim3(grid_of(grid)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -1,6 +1,6 @@
 // mxq_internal.h -- kernel argument tables and launchers shared by the C ABI
-// (mxq_api.hip) and the kernels (mxq_kernels.hip).  Not part of the public
-// interface.
+// (mxq_api.hip) and the kernels (mxq_grouped.hip, mxq_split.hip,
+// mxq_fused.hip).  Not part of the public interface.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,8 +49,8 @@ struct SplitArgs {
     const uint16_t *src;  // global row 0 of this launch's first split
     uint8_t *payload;     // same row
     uint8_t *scales;      // this launch's first split's scale region
-    float *row_amax;      // same row (may be null)
-    const float *g;
+    float *row_amax;      // same row (may be null unless row-scaled)
+    const float *g;       // NVFP4 encode scale; unused for MXFP8 and row-scaled
     int32_t cols;
     int32_t sf_cols;
     int32_t sf_stride;
@@ -88,14 +88,28 @@ struct SwizzleArgs {
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_grouped(int fmt, int layout, const GroupArgs &a, int64_t grid, hipStream_t s);
-hipError_t launch_split(int layout, const SplitArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,
+                        hipStream_t s);
 hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_swizzle(const SwizzleArgs &a, int64_t grid, hipStream_t s);
 
 // Largest supported row length (keeps one unit's staged scales within 32 KiB
-// of LDS and a fused row within registers).
+// of LDS, and a split or fused row within registers).
 constexpr int64_t kMaxColsMx = 32768;
 constexpr int64_t kMaxColsNv = 16384;
+constexpr int64_t kMaxSplitCols = 16384;
 constexpr int64_t kMaxFusedH = 16384;
+
+// Whole-row kernels (split, fused) keep half a row per wave in registers:
+// this many 512-column steps per wave.
+inline int half_row_steps(int64_t cols) {
+    const int64_t n = ((cols + kChunk - 1) / kChunk + 1) / 2;
+    if (n <= 1) return 1;
+    if (n <= 2) return 2;
+    if (n <= 4) return 4;
+    if (n <= 7) return 7;
+    if (n <= 8) return 8;
+    return 16;
+}
 
 }  // namespace mxq

@@ -1,0 +1,236 @@
+// mxq_split.hip -- quantize a concatenated routed activation once and split
+// it per expert: payload rows stay at their global rows, each expert's scales
+// go to its own, separately padded region of one bulk buffer, and the row
+// amax is emitted.  Three forms share the kernel: NVFP4 under one encode
+// scale, row-scaled NVFP4 (each row under an encode scale derived from its own
+// amax) and MXFP8.
+//
+// Swizzled: a unit owns line h (0..3) of every scale tile of one 128-row band
+// of one expert, i.e. the rows band*128 + 32*q + 8*h + i (q < 4, i < 8), so
+// its staged scales leave as whole 128-byte lines, padding rows and columns
+// zero.  Linear: a unit is 32 consecutive rows.  Only the unit's live rows are
+// loaded: pairs of waves take them in turn, each wave holding half of a row
+// (512-column steps 2k + half) in registers, so short experts keep every wave
+// busy.  A wave loads its next row only after storing the current one:
+// loading it earlier doubles the row registers and measured slower than
+// leaving the overlap to the other resident waves.  Units run in plain
+// dispatch order; every byte has one writer, and no global atomics are used.
+#include "mxq_device.h"
+#include "mxq_internal.h"
+
+namespace mxq {
+
+// Row-scaled NVFP4 encode scale of a row with amax a: 1 for an all-zero row,
+// else fp32(2688 / a) (IEEE division; 2688 = 448 * 6 maps the row amax onto
+// the largest block scale times the largest element) clamped to
+// [2^-100, 2^100], the range in which nv_scale's multipliers are exact.
+__device__ __forceinline__ float nv_row_encode_scale(float a) {
+    if (a == 0.0f) return 1.0f;
+    return __builtin_fminf(__builtin_fmaxf(2688.0f / a, 0x1p-100f), 0x1p100f);
+}
+
+// Up to 8 half-row steps fit in 128 VGPRs, so two workgroups share a CU;
+// wider rows get the whole register file.
+template <int FMT, bool ROWSC, int LAYOUT, int NCH2>
+__global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(NCH2 <= 8 ? 4 : 1)))
+void k_split(const SplitArgs a) {
+    using Tr = FmtTraits<FMT>;
+    extern __shared__ __align__(16) uint8_t stage[];
+    __shared__ uint32_t row_max[32];     // one encode scale: row amax folded by LDS atomics
+    __shared__ uint32_t half_max[2][8];  // row-scaled: each wave's half-row amax, two buffers
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int pair = w >> 1, half = w & 1;
+    const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
+    const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
+    const float g = (FMT == MXQ_NVFP4 && !ROWSC) ? *a.g : 0.0f;
+    const float quot = (FMT == MXQ_NVFP4 && !ROWSC) ? nv_wave_quot(g) : 0.0f;
+    const int stage_bytes = 32 * a.sf_stride;
+    int it = 0;  // row-scaled step counter, uniform over the workgroup
+    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
+        int lo = 0, hi = a.n;  // split s with unit_off[s] <= u < unit_off[s + 1]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.unit_off[mid] <= u) lo = mid; else hi = mid;
+        }
+        const int s = lo;
+        const int lu = u - a.unit_off[s];
+        const int m = a.row_off[s + 1] - a.row_off[s];
+        const int64_t e0 = a.row_off[s];  // expert's first row
+        // live rows of the unit, in order; nq[q] of them in line-set row q
+        int nq[4] = {0, 0, 0, 0};
+        int n_live;
+        int band = 0, h = 0;
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            band = lu >> 2;
+            h = lu & 3;
+            const int rb = min(128, m - band * 128);
+            n_live = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                nq[q] = min(8, max(0, rb - 32 * q - 8 * h));
+                n_live += nq[q];
+            }
+        } else {
+            n_live = min(32, m - lu * 32);
+        }
+        // j-th live row of the unit -> (line-set row q, slot i, row in expert)
+        auto locate = [&](int j, int &q, int &i) {
+            q = 0;
+            i = j;
+            if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+                while (i >= nq[q]) { i -= nq[q]; ++q; }
+                return band * 128 + 32 * q + 8 * h + i;
+            } else {
+                return lu * 32 + j;
+            }
+        };
+        auto load_row = [&](int j, u32x4 *v) {
+            int q, i;
+            const uint16_t *src = a.src + (e0 + locate(j, q, i)) * a.cols;
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
+                v[k] = u32x4{0, 0, 0, 0};
+                if (col < a.cols)
+                    v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + col));
+            }
+        };
+        u32x4 cur[NCH2];
+        // this wave's half-row amax (columns past the row were loaded as zeros)
+        auto half_amax = [&]() {
+            uint32_t am = 0;
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) am = max(am, amax_bits8(cur[k]));
+            return wave_max(am);
+        };
+        // encode the half row in cur as live row j under (gr, qr); whole wave.
+        // am accumulates the half row's amax bits over the live columns.
+        auto encode = [&](int j, float gr, float qr, uint32_t &am) {
+            int q, i;
+            const int r = locate(j, q, i);
+            uint8_t *pay_row = a.payload + (e0 + r) * payload_ld;
+#pragma unroll
+            for (int k = 0; k < NCH2; ++k) {
+                const int col = (2 * k + half) * kChunk + lane * 8;
+                u32x2 pay;
+                const uint32_t code = quant8<FMT>(cur[k], gr, qr, pay);
+                if (col < a.cols) {
+                    store_payload<FMT>(pay_row, col, pay);
+                    if (!ROWSC) am = max(am, amax_bits8(cur[k]));
+                    if (leader) {
+                        const int c = col / Tr::kBlock;
+                        if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+                            stage[(c >> 2) * 128 + i * 16 + q * 4 + (c & 3)] = (uint8_t)code;
+                        else
+                            stage[j * a.sf_cols + c] = (uint8_t)code;
+                    }
+                }
+            }
+            return r;
+        };
+
+        if (pair < n_live) load_row(pair, cur);
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            for (int k = threadIdx.x * 16; k < stage_bytes; k += kSplitThreads * 16)
+                *reinterpret_cast<u32x4 *>(stage + k) = u32x4{0, 0, 0, 0};
+        }
+        if (!ROWSC && threadIdx.x < 32) row_max[threadIdx.x] = 0;
+        __syncthreads();
+        if constexpr (!ROWSC) {
+            for (int j = pair; j < n_live; j += 4) {
+                uint32_t am = 0;
+                encode(j, g, quot, am);
+                am = wave_max(am);
+                if (lane == 0) atomicMax(&row_max[j], am);
+                if (j + 4 < n_live) load_row(j + 4, cur);
+            }
+        } else {
+            // Every wave takes every step (the barrier needs all of them); a
+            // row's two halves meet in half_max before either is encoded.
+            for (int j0 = 0; j0 < n_live; j0 += 4, ++it) {
+                const int j = j0 + pair;
+                const uint32_t am = j < n_live ? half_amax() : 0u;
+                if (lane == 0) half_max[it & 1][w] = am;
+                __syncthreads();
+                if (j < n_live) {
+                    const uint32_t ra = max(half_max[it & 1][2 * pair], half_max[it & 1][2 * pair + 1]);
+                    const float af = __uint_as_float(ra << 16);
+                    const float gr = nv_row_encode_scale(af);
+                    uint32_t unused = 0;
+                    const int r = encode(j, gr, nv_wave_quot(gr), unused);
+                    if (a.row_amax && half == 0 && lane == 0) a.row_amax[e0 + r] = af;
+                }
+                if (j + 4 < n_live) load_row(j + 4, cur);
+            }
+        }
+        __syncthreads();
+        if (!ROWSC && a.row_amax && (int)threadIdx.x < n_live) {
+            int q, i;
+            const int r = locate(threadIdx.x, q, i);
+            a.row_amax[e0 + r] = __uint_as_float(row_max[threadIdx.x] << 16);
+        }
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            const int tiles = a.sf_stride >> 2;
+            uint8_t *base = a.scales + (int64_t)(a.unit_off[s] >> 2) * tiles * 512 +
+                            (int64_t)band * tiles * 512 + h * 128;
+            for (int k = threadIdx.x; k < tiles * 8; k += kSplitThreads) {
+                const int t = k >> 3, part = k & 7;
+                *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512 + part * 16) =
+                    *reinterpret_cast<const u32x4 *>(stage + t * 128 + part * 16);
+            }
+        } else {
+            uint8_t *dst = a.scales + (e0 + lu * 32) * a.sf_cols;
+            const int nbytes = n_live * a.sf_cols;
+            if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                for (int k = threadIdx.x; k < (nbytes >> 4); k += kSplitThreads)
+                    *reinterpret_cast<u32x4 *>(dst + k * 16) =
+                        *reinterpret_cast<const u32x4 *>(stage + k * 16);
+                for (int k = (nbytes & ~15) + threadIdx.x; k < nbytes; k += kSplitThreads)
+                    dst[k] = stage[k];
+            } else {
+                for (int k = threadIdx.x; k < nbytes; k += kSplitThreads) dst[k] = stage[k];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launcher.
+// ---------------------------------------------------------------------------
+template <int FMT, bool ROWSC, int LAYOUT>
+static void split_nch(const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
+    const dim3 bd(kSplitThreads);
+    switch (half_row_steps(a.cols)) {
+    case 1: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 1>), gd, bd, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 2>), gd, bd, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 4>), gd, bd, lds, s, a); break;
+    case 7: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 7>), gd, bd, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 8>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 16>), gd, bd, lds, s, a); break;
+    }
+}
+
+template <int FMT, bool ROWSC>
+static void split_layout(int layout, const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
+    if (layout == MXQ_SF_LINEAR)
+        split_nch<FMT, ROWSC, MXQ_SF_LINEAR>(a, gd, lds, s);
+    else
+        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED>(a, gd, lds, s);
+}
+
+hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,
+                        hipStream_t s) {
+    const size_t lds = (size_t)32 * a.sf_stride;
+    const dim3 gd((unsigned)(grid < 1 ? 1 : grid));
+    if (fmt == MXQ_MXFP8)
+        split_layout<MXQ_MXFP8, false>(layout, a, gd, lds, s);
+    else if (row_scaled)
+        split_layout<MXQ_NVFP4, true>(layout, a, gd, lds, s);
+    else
+        split_layout<MXQ_NVFP4, false>(layout, a, gd, lds, s);
+    return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -33,8 +33,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"mx_quant_grouped", "nvfp4_quant_split", "rmsnorm_quant_fused",
-            "scale_swizzle"} <= set(names)
+    assert {"mx_quant_grouped", "nvfp4_quant_split", "nvfp4_quant_split_row_scaled",
+            "mxfp8_quant_split", "rmsnorm_quant_fused", "scale_swizzle"} <= set(names)
     L = ctypes.CDLL(mxq.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -126,6 +126,45 @@ def test_split_validation():
     assert _split([4], src=A + 4) == ESHAPE
     assert _split([4], sc=A + 1, layout=1) == ESHAPE
     assert _split([0, 0, 0], src=0, pay=0, sc=0, g=0) == OK   # all empty: no launch
+
+
+def _split_rows(split, T=None, cols=64, src=A, pay=A, sc=A, amax=A, layout=1):
+    T = sum(split) if T is None else T
+    arr = (ctypes.c_int64 * max(len(split), 1))(*split)
+    return mxq.lib().nvfp4_quant_split_row_scaled(src, T, cols, arr, len(split), pay, sc, amax,
+                                                  layout, None)
+
+
+def _split_mx(split, T=None, cols=64, src=A, pay=A, sc=A, amax=A, layout=1):
+    T = sum(split) if T is None else T
+    arr = (ctypes.c_int64 * max(len(split), 1))(*split)
+    return mxq.lib().mxfp8_quant_split(src, T, cols, arr, len(split), pay, sc, amax, layout, None)
+
+
+def test_split_modes_validation():
+    for f in (_split_rows, _split_mx):
+        assert f([3, 4], T=8) == EINVAL
+        assert f([3, -1, 4], T=6) == EINVAL
+        assert f([]) == EINVAL
+        assert f([4], layout=2) == EINVAL
+        assert f([4], cols=32768) == ESHAPE
+        assert f([4], src=0) == EINVAL
+        assert f([4], pay=0) == EINVAL
+        assert f([4], pay=A + 4) == ESHAPE
+        assert f([4], sc=A + 2) == ESHAPE
+        assert f([0, 0], src=0, pay=0, sc=0, amax=0) == OK
+    assert _split_rows([4], cols=40) == ESHAPE       # 40 % 16
+    assert _split_rows([4], cols=48, amax=0) == EINVAL  # row amax is required
+    assert _split_mx([4], cols=48) == ESHAPE          # 48 % 32
+    assert _split_mx([4], amax=0, src=0) == EINVAL    # row amax optional, src is not
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_mxfp8_split_offsets_match_oracle(orc, layout):
+    split = [0, 1, 127, 128, 129, 0, 255, 3]
+    for i in range(len(split) + 1):
+        assert mxq.split_scale_offset(split, i, 7168, 0, layout) == \
+            orc.split_scale_offset(split, i, 7168, orc.MXFP8, layout)
 
 
 def _fused(fmt=0, layout=1, T=4, H=256, eps=1e-6, x=A, g=0):
