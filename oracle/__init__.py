@@ -53,7 +53,8 @@ def _load(path):
         "orc_split": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _u16p, _i64, _i64, _i64p,
                                      ctypes.c_int, ctypes.c_float, ctypes.c_int, _u8p, _u8p,
                                      _f32p]),
-        "orc_nvfp4_row_encode_scale": (ctypes.c_float, [ctypes.c_float]),
+        "orc_nvfp4_encode_scale": (ctypes.c_float, [ctypes.c_float]),
+        "orc_tensor_amax": (ctypes.c_float, [_u16p, _i64, _i64, _i64]),
         "orc_add_rmsnorm": (ctypes.c_int, [_u16p, _u16p, _u16p, ctypes.c_float, _i64, _i64,
                                            _u16p, _u16p]),
         "orc_scale_swizzle": (ctypes.c_int, [_u8p, _i64, _i64, _u8p]),
@@ -214,7 +215,7 @@ def nvfp4_split(src_bits, split_rows, g, layout):
 def split(fmt, src_bits, split_rows, g=1.0, layout=LINEAR, row_scaled=False):
     """Split quantization in any mode: MXFP8 (g ignored), NVFP4 under one
     encode scale g, or row-scaled NVFP4 (each row under
-    nvfp4_row_encode_scale of its own amax).
+    nvfp4_encode_scale of its own amax).
 
     Returns (payload [T, cols or cols/2], bulk scales, row_amax fp32 [T])."""
     src = np.ascontiguousarray(src_bits, dtype=np.uint16)
@@ -232,8 +233,31 @@ def split(fmt, src_bits, split_rows, g=1.0, layout=LINEAR, row_scaled=False):
     return payload, scales, amax
 
 
-def nvfp4_row_encode_scale(amax):
-    return lib().orc_nvfp4_row_encode_scale(float(amax))
+def nvfp4_encode_scale(amax):
+    return lib().orc_nvfp4_encode_scale(float(amax))
+
+
+def tensor_amax(src_bits, cols=None):
+    src = np.ascontiguousarray(src_bits, dtype=np.uint16)
+    rows, ld = src.shape
+    return lib().orc_tensor_amax(_ptr(src, _u16p), rows, ld if cols is None else cols, ld)
+
+
+def quantize_auto(layout, srcs, slots=None, cols=None):
+    """Grouped NVFP4 with encode scales from the data: entry i belongs to
+    scale slot slots[i] (default: its own); a slot's amax is the max over its
+    entries, its encode scale nvfp4_encode_scale(amax), and every entry is
+    quantized under its slot's scale.
+
+    Returns (payloads, scales, g [n_slots] fp32, amax [n_slots] fp32)."""
+    slots = list(range(len(srcs))) if slots is None else list(slots)
+    n_slots = max(slots) + 1
+    amax = np.zeros(n_slots, np.float32)
+    for s, x in zip(slots, srcs):
+        amax[s] = max(amax[s], tensor_amax(x, cols))
+    g = np.array([nvfp4_encode_scale(a) for a in amax], np.float32)
+    outs = [quantize(NVFP4, layout, x, cols, float(g[s])) for s, x in zip(slots, srcs)]
+    return [o[0] for o in outs], [o[1] for o in outs], g, amax
 
 
 def add_rmsnorm(x_bits, res_bits, gamma_bits, eps):

@@ -338,16 +338,18 @@ int64_t orc_split_scale_offset(const int64_t *split_rows, int n, int i, int64_t 
     return off;
 }
 
-/* Row-scaled NVFP4 [TE-3800, Description: the activation's second-level
- * scale is per row and derived from that row's amax].  The pages do not print
- * the formula; the per-tensor convention (an encode scale that maps the amax
- * onto the largest E4M3 block scale 448 times the largest E2M1 element 6)
- * applied to one row gives g_r = fp32(2688 / a), a correctly rounded fp32
- * division.  An all-zero row takes g_r = 1 (any value quantizes it to zeros),
- * and g_r is clamped to [2^-100, 2^100], the range in which every block
- * multiplier g_r / s_q stays a finite normal fp32 number; rows reach the
- * clamp only when a < 2688 * 2^-100 or a > 2688 * 2^100. */
-float orc_nvfp4_row_encode_scale(float amax)
+/* NVFP4 encode scale from an amax a, for a whole tensor [MO-2750, review: a
+ * per-expert second-level scale, one for the fused gate/up pair since they
+ * share one amax] or for one row of a row-scaled activation [TE-3800,
+ * Description: the second-level scale is per row, from the row amax].  The
+ * pages print no formula; the convention that maps the amax onto the largest
+ * E4M3 block scale (448) times the largest E2M1 element (6) gives
+ * g = fp32(2688 / a), a correctly rounded fp32 division.  An all-zero input
+ * takes g = 1 (any value quantizes it to zeros), and g is clamped to
+ * [2^-100, 2^100], the range in which every block multiplier g / s_q stays a
+ * finite normal fp32 number; only a < 2688 * 2^-100 or a > 2688 * 2^100
+ * reach the clamp. */
+float orc_nvfp4_encode_scale(float amax)
 {
     float g, lo = (float)ldexp(1.0, -100), hi = (float)ldexp(1.0, 100);
     assert(amax >= 0.0f && isfinite(amax));
@@ -359,6 +361,20 @@ float orc_nvfp4_row_encode_scale(float amax)
     if (g > hi)
         g = hi;
     return g;
+}
+
+float orc_tensor_amax(const uint16_t *src, int64_t rows, int64_t cols, int64_t ld)
+{
+    double amax = 0.0;
+    int64_t r, j;
+    for (r = 0; r < rows; ++r)
+        for (j = 0; j < cols; ++j) {
+            double v = fabs(orc_bf16_value(src[r * ld + j]));
+            assert(isfinite(v));
+            if (v > amax)
+                amax = v;
+        }
+    return (float)amax; /* exact: a bf16 value */
 }
 
 static float row_amax_of(const uint16_t *x, int64_t cols)
@@ -407,7 +423,7 @@ int orc_split(int fmt, int row_scaled, const uint16_t *src, int64_t total_rows, 
             memset(scales + base, 0, (size_t)orc_sf_bytes(m, C, layout));
             for (r = 0; r < m; ++r) {
                 const uint16_t *x = src + (o + r) * cols;
-                float gr = orc_nvfp4_row_encode_scale(row_amax_of(x, cols));
+                float gr = orc_nvfp4_encode_scale(row_amax_of(x, cols));
                 int64_t c;
                 for (c = 0; c < C; ++c) {
                     uint8_t sc;

@@ -78,13 +78,15 @@ int orc_nvfp4_split(const uint16_t *src, int64_t total_rows, int64_t cols,
                     const int64_t *split_rows, int n, float g, int layout,
                     uint8_t *payload, uint8_t *scales, float *row_amax);
 /* Any format: MXFP8 (g ignored), NVFP4 under one encode scale g, or, with
- * row_scaled != 0, NVFP4 where row r uses orc_nvfp4_row_encode_scale(row_amax[r]). */
+ * row_scaled != 0, NVFP4 where row r uses orc_nvfp4_encode_scale(row_amax[r]). */
 int orc_split(int fmt, int row_scaled, const uint16_t *src, int64_t total_rows, int64_t cols,
               const int64_t *split_rows, int n, float g, int layout, uint8_t *payload,
               uint8_t *scales, float *row_amax);
-/* Per-row NVFP4 encode scale: 1 for a zero row, else fp32(2688 / amax)
- * clamped to [2^-100, 2^100]. */
-float orc_nvfp4_row_encode_scale(float amax);
+/* NVFP4 encode scale from an amax (a tensor's or a row's): 1 for amax 0,
+ * else fp32(2688 / amax) clamped to [2^-100, 2^100]. */
+float orc_nvfp4_encode_scale(float amax);
+/* max |x| over a bf16 [rows, cols] tensor with row stride ld. */
+float orc_tensor_amax(const uint16_t *src, int64_t rows, int64_t cols, int64_t ld);
 
 /* Residual add + RMSNorm: residual_out = bf16(x + res);
  * norm_out = bf16(r * gamma / sqrt(mean(r^2) + eps)), computed in double. */

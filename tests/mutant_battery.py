@@ -18,6 +18,7 @@ import oracle  # noqa: E402
 import test_oracle_blocks as B  # noqa: E402
 import test_oracle_formats as F  # noqa: E402
 import test_oracle_split_modes as S  # noqa: E402
+import test_oracle_auto_scale as A  # noqa: E402
 from helpers import hand_blocks, row_scaled_rows  # noqa: E402
 
 
@@ -48,6 +49,10 @@ def checks():
     yield "row_split_indep", S.test_row_scaled_rows_independent_of_split
     yield "mx_split_sizes", S.test_mxfp8_split_sizes_by_hand
     yield "mx_split", S.test_mxfp8_split_equals_per_expert
+    yield "tensor_amax", A.test_tensor_amax_matches_numpy
+    yield "auto_scale", A.test_auto_equals_per_tensor_with_numpy_scale
+    yield "auto_shared", A.test_shared_slot_takes_the_larger_amax
+    yield "auto_six", A.test_slot_amax_element_encodes_as_six
     yield "rmsnorm", lambda o: [B.test_add_rmsnorm_pins(o, sc) for sc in (1.0, 1e-3)]
 
 

@@ -59,6 +59,10 @@ MUTANTS = [
     ("split_payload_row_width_nvfp4",
      "int64_t payload_row = fmt == ORC_MXFP8 ? cols : cols / 2;\n    int64_t C;",
      "int64_t payload_row = cols / 2;\n    int64_t C;"),
+    ("tensor_amax_ignores_stride", "double v = fabs(orc_bf16_value(src[r * ld + j]));",
+     "double v = fabs(orc_bf16_value(src[r * cols + j]));"),
+    ("tensor_amax_signed", "            double v = fabs(orc_bf16_value(src[r * ld + j]));",
+     "            double v = orc_bf16_value(src[r * ld + j]);"),
 ]
 
 

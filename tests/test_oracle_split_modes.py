@@ -20,7 +20,7 @@ ROWS = row_scaled_rows()
 def test_row_scaled_hand_row(orc, case):
     x = np.array(case["x"], np.uint16).reshape(1, 32)
     amax_val = orc.bf16_value(case["amax"])
-    assert orc.nvfp4_row_encode_scale(amax_val) == np.float32(case["g"])
+    assert orc.nvfp4_encode_scale(amax_val) == np.float32(case["g"])
     for layout in (orc.LINEAR, orc.SWIZZLED):
         payload, scales, amax = orc.split(orc.NVFP4, x, [1], layout=layout, row_scaled=True)
         assert list(payload[0]) == case["payload"]
@@ -35,19 +35,19 @@ def test_row_scaled_hand_row(orc, case):
 
 
 def test_row_encode_scale_special_values(orc):
-    assert orc.nvfp4_row_encode_scale(0.0) == 1.0
-    assert orc.nvfp4_row_encode_scale(2688.0) == 1.0
-    assert orc.nvfp4_row_encode_scale(1.0) == 2688.0
-    assert orc.nvfp4_row_encode_scale(7.0) == 384.0
+    assert orc.nvfp4_encode_scale(0.0) == 1.0
+    assert orc.nvfp4_encode_scale(2688.0) == 1.0
+    assert orc.nvfp4_encode_scale(1.0) == 2688.0
+    assert orc.nvfp4_encode_scale(7.0) == 384.0
     # clamp edges: 2688 * 2^-100 and 2688 * 2^100 are the largest / smallest
     # amax values that do not clamp
     lo = 2688.0 * 2.0 ** -100
     hi = 2688.0 * 2.0 ** 100
-    assert orc.nvfp4_row_encode_scale(lo) == 2.0 ** 100
-    assert orc.nvfp4_row_encode_scale(lo / 2) == 2.0 ** 100
-    assert orc.nvfp4_row_encode_scale(hi) == 2.0 ** -100
-    assert orc.nvfp4_row_encode_scale(hi * 2) == 2.0 ** -100
-    assert orc.nvfp4_row_encode_scale(3.0 * 2.0 ** 50) == np.float32(896.0 * 2.0 ** -50)
+    assert orc.nvfp4_encode_scale(lo) == 2.0 ** 100
+    assert orc.nvfp4_encode_scale(lo / 2) == 2.0 ** 100
+    assert orc.nvfp4_encode_scale(hi) == 2.0 ** -100
+    assert orc.nvfp4_encode_scale(hi * 2) == 2.0 ** -100
+    assert orc.nvfp4_encode_scale(3.0 * 2.0 ** 50) == np.float32(896.0 * 2.0 ** -50)
 
 
 def _rows(T, H, seed, scale_spread=1.0):
