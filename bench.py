@@ -264,37 +264,79 @@ def extra_workloads(torch, mxq, workloads, dev):
         "overhead_per_extra_launch_us": round((ts - tg) / (len(single) - len(grouped)) * 1e6, 2)}
     del layer, grouped, single
 
-    # routed activation split, NVFP4 swizzled, 8 rotating input copies (> MALL)
+    # NVFP4 with encode scales from the data, same call (amax pass + quantize):
+    # one Qwen3-235B-A22B gate_up launch of 16 experts, swizzled
+    r, c = workloads.QWEN3_235B_A22B["gate_up"]
+    stack = workloads.expert_stack(G, r, c, std=0.015, seed=5000, device=dev)
+    auto = mxq.GroupedAutoCall(1, [stack[i] for i in range(G)])
+    gs = workloads.encode_scale_from_amax(stack.float().abs().amax(dim=(1, 2))).contiguous()
+    plain = mxq.GroupedCall(1, 1, [stack[i] for i in range(G)], auto.payloads, auto.scales, gs)
+
+    def torch_amax_then_grouped(i):
+        a = torch.linalg.vector_norm(stack, ord=float("inf"), dim=(1, 2)).float()
+        gs.copy_(torch.where(a > 0, 2688.0 / a, torch.ones_like(a)))
+        plain()
+    ta = timed(torch, lambda i: auto(), 20)
+    tp = timed(torch, lambda i: plain(), 20)
+    tt = timed(torch, torch_amax_then_grouped, 20)
+    nb = G * (r * c * 2 + r * c // 2 + mxq.scale_bytes(r, c, 1, 1) + 8)
+    res["nvfp4_auto_scale_qwen3_235b_gate_up_16x3072x4096"] = {
+        "alg_bytes": nb, "hbm_bytes_two_pass": nb + G * r * c * 2,
+        "auto_us": round(ta * 1e6, 1), "auto_GBps_alg": round(nb / ta / 1e9, 1),
+        "auto_GBps_two_pass": round((nb + G * r * c * 2) / ta / 1e9, 1),
+        "precomputed_g_us": round(tp * 1e6, 1),
+        "torch_amax_then_grouped_us": round(tt * 1e6, 1)}
+    del stack, auto, plain
+
+    # routed activation split, 8 rotating input copies (> MALL): NVFP4 with one
+    # encode scale, row-scaled NVFP4, MXFP8; linear and swizzled scales
     x, split = workloads.routed_activation()
     xs = [x.to(dev) for _ in range(8)]
     g = workloads.encode_scale_from_amax(xs[0].float().abs().amax()).reshape(1)
     T, H = x.shape
-    total = mxq.split_scale_offset(split, len(split), H)
-    pay = torch.empty(T, H // 2, dtype=torch.uint8, device=dev)
-    sc = torch.empty(total, dtype=torch.uint8, device=dev)
     am = torch.empty(T, dtype=torch.float32, device=dev)
-    t = timed(torch, lambda i: mxq.nvfp4_quant_split(xs[i % 8], split, g, 1, pay, sc, am), 20)
-    nb = T * H * 2 + T * H // 2 + total + 4 * T + 4
-    res["split_nvfp4_8192x7168_256experts"] = {"us": round(t * 1e6, 1), "alg_bytes": nb,
-                                                "GBps": round(nb / t / 1e9, 1)}
+    splits = {}
+    for mode, fmt in (("nvfp4", 1), ("nvfp4_row_scaled", 1), ("mxfp8", 0)):
+        pay = torch.empty(T, H if fmt == 0 else H // 2, dtype=torch.uint8, device=dev)
+        for layout, lname in ((0, "linear"), (1, "swizzled")):
+            total = mxq.split_scale_offset(split, len(split), H, fmt, layout)
+            sc = torch.empty(total, dtype=torch.uint8, device=dev)
+            if mode == "nvfp4":
+                fn = lambda i: mxq.nvfp4_quant_split(xs[i % 8], split, g, layout, pay, sc, am)
+            elif mode == "nvfp4_row_scaled":
+                fn = lambda i: mxq.nvfp4_quant_split_row_scaled(xs[i % 8], split, layout, pay, sc, am)
+            else:
+                fn = lambda i: mxq.mxfp8_quant_split(xs[i % 8], split, layout, pay, sc, am)
+            t = timed(torch, fn, 20)
+            nb = T * H * 2 + pay.numel() + total + 4 * T + (4 if mode == "nvfp4" else 0)
+            splits[f"{mode}_{lname}"] = {"us": round(t * 1e6, 1), "alg_bytes": nb,
+                                         "GBps": round(nb / t / 1e9, 1)}
+    res["split_8192x7168_256experts"] = splits
     del xs
 
-    # fused residual + RMSNorm + MXFP8 (swizzled), with the same-run e4m3 cast reference
-    sweep = {}
-    for T in (1, 16, 64, 256, 1024, 4096):
-        H = 7168
-        ins = [workloads.epilogue_inputs(T, H, seed=4000 + T + k, device=dev) for k in range(4)]
-        nsc = mxq.scale_bytes(T, H, 0, 1)
-        outs = (torch.empty(T, H, dtype=torch.bfloat16, device=dev),
-                torch.empty(T, H, dtype=torch.bfloat16, device=dev),
-                torch.empty(T, H, dtype=torch.uint8, device=dev),
-                torch.empty(nsc, dtype=torch.uint8, device=dev))
-        t = timed(torch, lambda i: mxq.rmsnorm_quant_fused(*ins[i % 4], 1e-6, 0, 1, out=outs), 50)
-        tc = timed(torch, lambda i: ins[i % 4][0].to(torch.float8_e4m3fn), 50)
-        nb = T * H * 9 + nsc + 2 * H
-        sweep[str(T)] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1),
-                         "e4m3_cast_us": round(tc * 1e6, 2)}
-    res["fused_rmsnorm_mxfp8_H7168"] = sweep
+    # fused residual + RMSNorm + quantize (swizzled), MXFP8 and NVFP4, with the
+    # same-run e4m3 cast reference
+    for fmt, fname in ((0, "mxfp8"), (1, "nvfp4")):
+        sweep = {}
+        for T in (1, 16, 64, 256, 1024, 4096):
+            H = 7168
+            ins = [workloads.epilogue_inputs(T, H, seed=4000 + T + k, device=dev) for k in range(4)]
+            nsc = mxq.scale_bytes(T, H, fmt, 1)
+            pw = H if fmt == 0 else H // 2
+            outs = (torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                    torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                    torch.empty(T, pw, dtype=torch.uint8, device=dev),
+                    torch.empty(nsc, dtype=torch.uint8, device=dev))
+            gf = torch.ones(1, dtype=torch.float32, device=dev)
+            t = timed(torch, lambda i: mxq.rmsnorm_quant_fused(*ins[i % 4], 1e-6, fmt, 1,
+                                                                 global_scale=gf, out=outs), 50)
+            nb = T * H * 8 + T * pw + nsc + 2 * H + (4 if fmt == 1 else 0)
+            entry = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
+            if fmt == 0:
+                tc = timed(torch, lambda i: ins[i % 4][0].to(torch.float8_e4m3fn), 50)
+                entry["e4m3_cast_us"] = round(tc * 1e6, 2)
+            sweep[str(T)] = entry
+        res[f"fused_rmsnorm_{fname}_H7168"] = sweep
 
     # small grouped case: 8 x [256,512] MXFP8 linear (launch-bound)
     xs8 = [x.to(dev) for x in workloads.small_grouped_experts(seed=0)]

@@ -106,6 +106,31 @@ int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries
                      void *stream);
 
 /*
+ * nvfp4_quant_grouped_auto -- mx_quant_grouped for NVFP4 with the encode
+ * scales computed from the data in the same call [MO-2750, review: the
+ * second-level scale is a per-expert scalar, shared by gate and up because
+ * the fused gate/up slice has one amax].  Entry i belongs to scale slot
+ * scale_slot[i]; a slot's amax is the max |x| over all of its entries and its
+ * encode scale is
+ *     g_s = 1 if amax_s = 0, else clamp(fp32(2688 / amax_s), 2^-100, 2^100)
+ * (2688 = 448 * 6; the pages print no formula).  Every entry is then
+ * quantized exactly as mx_quant_grouped(MXQ_NVFP4, ...) with g = g_s of its
+ * slot.  entries[i].global_scale is ignored.
+ *   scale_slot        host int[n_entries], values in [0, n_slots), or NULL
+ *                     for one slot per entry (then n_slots == n_entries)
+ *   n_slots           1..16
+ *   global_scale_out  device fp32 [n_slots]: g_s (every slot written; a slot
+ *                     with no rows gets amax 0 and g 1)
+ *   amax_out          device fp32 [n_slots]: amax_s; also the reduction's
+ *                     accumulator, so it must not alias anything else
+ * Three kernels on `stream` (zero the accumulators, per-slot amax, quantize):
+ * the input is read twice.  On MXQ_ELAUNCH the outputs are unspecified.
+ */
+int nvfp4_quant_grouped_auto(int layout, int64_t cols, const mxq_entry *entries, int n_entries,
+                             const int *scale_slot, int n_slots, float *global_scale_out,
+                             float *amax_out, void *stream);
+
+/*
  * nvfp4_quant_split -- quantize a concatenated routed activation once and
  * split it per expert [TE-3800, Description; Changes: independent per-expert
  * scale padding including uneven and empty splits; requantizing one expert

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         i64, vp, ci, cf = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         sigs = {
             "mx_quant_grouped": (ci, [ci, ci, i64, ctypes.POINTER(_Entry), ci, vp]),
+            "nvfp4_quant_grouped_auto": (ci, [ci, i64, ctypes.POINTER(_Entry), ci,
+                                              ctypes.POINTER(ci), ci, vp, vp, vp]),
             "nvfp4_quant_split": (ci, [vp, i64, i64, ctypes.POINTER(i64), ci, vp, vp, vp, vp,
                                        ci, vp]),
             "nvfp4_quant_split_row_scaled": (ci, [vp, i64, i64, ctypes.POINTER(i64), ci, vp, vp,
@@ -191,6 +193,72 @@ class GroupedCall:
             _check(L.mx_quant_grouped(self.fmt, self.layout, self.cols, ents, n, stream),
                    "mx_quant_grouped")
         return self.payloads, self.scales
+
+
+class GroupedAutoCall:
+    """nvfp4_quant_grouped_auto with its descriptor tables built once: NVFP4
+    with per-slot encode scales computed from the data in the same call.
+
+    slots: scale slot of each src (default: one per src).  Shared slots (the
+    gate and up of one expert) must fall within one call of at most 16
+    entries, so with shared slots len(srcs) <= 16; without, srcs are taken 16
+    per call.  Calling returns (payloads, scales, g [n_slots], amax [n_slots])."""
+
+    def __init__(self, layout, srcs, slots=None, payloads=None, scales=None, g_out=None,
+                 amax_out=None):
+        self.layout = layout
+        self.srcs = list(srcs)
+        n = len(self.srcs)
+        dummy_g = torch.ones(1, dtype=torch.float32, device=self.srcs[0].device)
+        self.payloads, self.scales = _grouped_outputs(NVFP4, layout, self.srcs, payloads, scales,
+                                                      dummy_g.expand(n).contiguous())
+        if slots is not None:
+            slots = [int(v) for v in slots]
+            if n > MAX_GROUP or len(slots) != n or min(slots) < 0:
+                raise ValueError("shared scale slots: at most 16 srcs, one slot index each")
+            n_slots = max(slots) + 1
+        else:
+            n_slots = n
+        dev = self.srcs[0].device
+        self.g = torch.empty(n_slots, dtype=torch.float32, device=dev) if g_out is None else g_out
+        self.amax = (torch.empty(n_slots, dtype=torch.float32, device=dev)
+                     if amax_out is None else amax_out)
+        _need_gpu(self.g, "g_out", torch.float32)
+        _need_gpu(self.amax, "amax_out", torch.float32)
+        if self.g.numel() < n_slots or self.amax.numel() < n_slots:
+            raise ValueError("g_out and amax_out need one value per slot")
+        self.cols = self.srcs[0].shape[1]
+        self.device = dev
+        self._batches = []
+        for b in range(0, n, MAX_GROUP):
+            m = min(MAX_GROUP, n - b)
+            ents = (_Entry * m)()
+            for j in range(m):
+                i = b + j
+                x = self.srcs[i]
+                ents[j] = _Entry(x.data_ptr(), self.payloads[i].data_ptr(),
+                                 self.scales[i].data_ptr(), None, x.shape[0], x.stride(0))
+            if slots is not None:
+                sl, ns, off = (ctypes.c_int * m)(*slots), n_slots, 0
+            else:
+                sl, ns, off = None, m, b
+            self._batches.append((ents, m, sl, ns, self.g.data_ptr() + 4 * off,
+                                  self.amax.data_ptr() + 4 * off))
+
+    def __call__(self, stream: Optional[ctypes.c_void_p] = None):
+        stream = _stream(self.device) if stream is None else stream
+        L = lib()
+        for ents, m, sl, ns, gp, ap in self._batches:
+            _check(L.nvfp4_quant_grouped_auto(self.layout, self.cols, ents, m, sl, ns, gp, ap,
+                                              stream), "nvfp4_quant_grouped_auto")
+        return self.payloads, self.scales, self.g, self.amax
+
+
+def nvfp4_quant_grouped_auto(layout: int, srcs: Sequence[torch.Tensor], slots=None,
+                             payloads=None, scales=None, g_out=None, amax_out=None):
+    """NVFP4 grouped quantization with encode scales from the data (see
+    GroupedAutoCall).  Returns (payloads, scales, g, amax)."""
+    return GroupedAutoCall(layout, srcs, slots, payloads, scales, g_out, amax_out)()
 
 
 def _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales):

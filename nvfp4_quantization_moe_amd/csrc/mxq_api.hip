@@ -72,13 +72,18 @@ int64_t mxq_split_scale_offset(const int64_t *split_rows, int n_splits, int i, i
     return off;
 }
 
-int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries, int n_entries,
-                     void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validate and pack a grouped call.  Returns MXQ_OK and fills `a`, or the
+// status of the first failed check.
+int pack_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries, int n_entries,
+                 bool need_g, GroupArgs &a) {
     if (!valid_fmt(fmt) || !valid_layout(layout) || !entries || n_entries < 1 ||
         n_entries > MXQ_MAX_GROUP)
         return MXQ_EINVAL;
     if (cols <= 0 || cols % block_of(fmt) != 0 || cols > max_cols(fmt)) return MXQ_ESHAPE;
-    GroupArgs a;
     memset(&a, 0, sizeof(a));
     a.n = n_entries;
     a.cols = (int32_t)cols;
@@ -91,7 +96,7 @@ int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries
         if (e.rows < 0 || e.rows >= (int64_t)1 << 31) return MXQ_EINVAL;
         if (e.rows > 0) {
             if (!e.src || !e.payload || !e.scales) return MXQ_EINVAL;
-            if (fmt == MXQ_NVFP4 && !e.global_scale) return MXQ_EINVAL;
+            if (need_g && !e.global_scale) return MXQ_EINVAL;
             if (e.src_ld < cols || e.src_ld % 8 != 0 || e.src_ld >= (int64_t)1 << 31)
                 return MXQ_ESHAPE;
             if (!aligned16(e.src) || !aligned16(e.payload)) return MXQ_ESHAPE;
@@ -104,12 +109,54 @@ int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries
         a.e[i].ld = e.src_ld;
         a.e[i].rows = (int32_t)e.rows;
         a.e[i].unit_begin = (int32_t)units;
+        a.e[i].slot = i;
         units += row_groups(e.rows, layout, kUnitRows) * a.n_cc;
         if (units >= (int64_t)1 << 31) return MXQ_ESHAPE;
     }
     a.total_units = (int32_t)units;
-    if (units == 0) return MXQ_OK;
-    hipError_t err = launch_grouped(fmt, layout, a, grid_for(units), (hipStream_t)stream);
+    return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries, int n_entries,
+                     void *stream) {
+    GroupArgs a;
+    const int st = pack_grouped(fmt, layout, cols, entries, n_entries, fmt == MXQ_NVFP4, a);
+    if (st != MXQ_OK) return st;
+    if (a.total_units == 0) return MXQ_OK;
+    hipError_t err =
+        launch_grouped(fmt, layout, false, a, grid_for(a.total_units), (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;
+}
+
+int nvfp4_quant_grouped_auto(int layout, int64_t cols, const mxq_entry *entries, int n_entries,
+                             const int *scale_slot, int n_slots, float *global_scale_out,
+                             float *amax_out, void *stream) {
+    GroupArgs a;
+    const int st = pack_grouped(MXQ_NVFP4, layout, cols, entries, n_entries, false, a);
+    if (st != MXQ_OK) return st;
+    if (n_slots < 1 || n_slots > MXQ_MAX_GROUP || !global_scale_out || !amax_out)
+        return MXQ_EINVAL;
+    if (!scale_slot && n_slots != n_entries) return MXQ_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(global_scale_out) & 3) != 0 ||
+        (reinterpret_cast<uintptr_t>(amax_out) & 3) != 0)
+        return MXQ_ESHAPE;
+    for (int i = 0; i < n_entries; ++i) {
+        const int sl = scale_slot ? scale_slot[i] : i;
+        if (sl < 0 || sl >= n_slots) return MXQ_EINVAL;
+        a.e[i].slot = sl;
+    }
+    a.amax_bits = reinterpret_cast<uint32_t *>(amax_out);
+    a.g_out = global_scale_out;
+    a.n_slots = n_slots;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t grid = grid_for(a.total_units);
+    if (launch_amax(a, grid, s) != hipSuccess) return MXQ_ELAUNCH;
+    // the quantize pass always runs: its workgroup 0 publishes the encode scales
+    hipError_t err = launch_grouped(MXQ_NVFP4, layout, true, a, grid, s);
     return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;
 }
 

@@ -173,6 +173,15 @@ __device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g, float 
     return r;
 }
 
+// NVFP4 encode scale from an amax a (a tensor's, a scale slot's or a row's):
+// 1 when a = 0, else fp32(2688 / a) (IEEE division; 2688 = 448 * 6 maps the
+// amax onto the largest block scale times the largest element) clamped to
+// [2^-100, 2^100], the range in which nv_scale's multipliers are exact.
+__device__ __forceinline__ float nv_encode_scale(float a) {
+    if (a == 0.0f) return 1.0f;
+    return __builtin_fminf(__builtin_fmaxf(2688.0f / a, 0x1p-100f), 0x1p100f);
+}
+
 // Quantize 8 bf16 values with multiplier m; returns 4 bytes of packed E2M1
 // (element 2j in the low nibble of byte j).  fp32(x * m) is formed first;
 // v_cvt_scalef32_pk_fp4_f32 with scale 1.0 then rounds each fp32 to E2M1

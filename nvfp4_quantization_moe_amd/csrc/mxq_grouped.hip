@@ -41,7 +41,10 @@ __device__ __forceinline__ int group_row(int rg, int q, int i) {
         return rg * kUnitRows + kRowsPerWave * q + i;
 }
 
-template <int FMT, int LAYOUT>
+// AUTO (NVFP4 only): the encode scale of entry e is nv_encode_scale of its
+// slot's amax, reduced beforehand by k_amax; workgroup 0 publishes every
+// slot's encode scale.
+template <int FMT, int LAYOUT, bool AUTO>
 __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
     using Tr = FmtTraits<FMT>;
     constexpr int kCodes = kChunk / Tr::kBlock;  // scale codes per row per unit: 16 or 32
@@ -52,6 +55,8 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
     const int cl = lane * 8 / Tr::kBlock;  // this lane's code column inside the unit
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
+    if (AUTO && blockIdx.x == 0 && (int)threadIdx.x < a.n_slots)
+        a.g_out[threadIdx.x] = nv_encode_scale(__uint_as_float(a.amax_bits[threadIdx.x]));
     for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
         int ei = 0;
         while (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) ++ei;
@@ -61,7 +66,9 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
         const int cc = lu - rg * a.n_cc;
         const int col = cc * kChunk + lane * 8;
         const bool live_col = col < a.cols;
-        const float g = FMT == MXQ_NVFP4 ? *E.g : 0.0f;
+        const float g = FMT != MXQ_NVFP4 ? 0.0f
+                        : AUTO ? nv_encode_scale(__uint_as_float(a.amax_bits[E.slot]))
+                               : *E.g;
         const float quot = FMT == MXQ_NVFP4 ? nv_wave_quot(g) : 0.0f;
 
         u32x4 v[kRowsPerWave];
@@ -131,20 +138,102 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Per-slot amax for encode scales from the data.  A workgroup folds a run of
+// kAmaxUnits consecutive k_grouped units into one value per slot and makes
+// one atomic max per slot it touched: atomics on one address from every
+// workgroup serialize (one per unit measured 4x slower than the whole read),
+// so the run length sets their number.  The amax is kept as fp32 bits (a
+// bf16 magnitude shifted up), whose unsigned order is the value order.  The
+// quantize pass reads the input again from HBM: walking the units in either
+// order, in calls of 1 to 16 experts, showed no reuse from the last-level
+// cache.
+// ---------------------------------------------------------------------------
+constexpr int kAmaxUnits = 16;
+
+__global__ __launch_bounds__(64) void k_zero_slots(uint32_t *amax_bits, int n) {
+    if ((int)threadIdx.x < n) amax_bits[threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void k_amax(const GroupArgs a) {
+    __shared__ uint32_t red[kThreads / kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = threadIdx.x >> 6;
+    // fold the workgroup's running max m into slot `slot` (uniform call)
+    auto flush = [&](uint32_t m, int slot) {
+        m = wave_max(m);
+        if (lane == 0) red[q] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            m = max(max(red[0], red[1]), max(red[2], red[3]));
+            if (m != 0) atomicMax(a.amax_bits + slot, m << 16);
+        }
+        __syncthreads();
+    };
+    const int n_runs = (a.total_units + kAmaxUnits - 1) / kAmaxUnits;
+    for (int run = blockIdx.x; run < n_runs; run += gridDim.x) {
+        const int lo = run * kAmaxUnits;  // units [lo, hi)
+        const int hi = min(a.total_units, lo + kAmaxUnits);
+        int ei = 0;
+        while (ei + 1 < a.n && lo >= a.e[ei + 1].unit_begin) ++ei;
+        int slot = a.e[ei].slot;
+        uint32_t m = 0;
+        for (int u = lo; u < hi; ++u) {
+            if (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) {  // crossed into a later entry
+                while (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) ++ei;
+                if (a.e[ei].slot != slot) {
+                    flush(m, slot);
+                    m = 0;
+                    slot = a.e[ei].slot;
+                }
+            }
+            const GEntry &E = a.e[ei];
+            const int lu = u - E.unit_begin;
+            const int rg = lu / a.n_cc;
+            const int col = (lu - rg * a.n_cc) * kChunk + lane * 8;
+            u32x4 v[kRowsPerWave];
+#pragma unroll
+            for (int i = 0; i < kRowsPerWave; ++i) {
+                const int r = rg * kUnitRows + kRowsPerWave * q + i;
+                v[i] = u32x4{0, 0, 0, 0};
+                if (r < E.rows && col < a.cols)
+                    v[i] = *reinterpret_cast<const u32x4 *>(E.src + (int64_t)r * E.ld + col);
+            }
+#pragma unroll
+            for (int i = 0; i < kRowsPerWave; ++i) m = max(m, amax_bits8(v[i]));
+        }
+        flush(m, slot);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launcher.
 // ---------------------------------------------------------------------------
 static inline unsigned grid_of(int64_t g) { return (unsigned)(g < 1 ? 1 : g); }
 
-hipError_t launch_grouped(int fmt, int layout, const GroupArgs &a, int64_t grid, hipStream_t s) {
+hipError_t launch_grouped(int fmt, int layout, bool auto_scale, const GroupArgs &a, int64_t grid,
+                          hipStream_t s) {
     const dim3 gd(grid_of(grid)), bd(kThreads);
     if (fmt == MXQ_MXFP8 && layout == MXQ_SF_LINEAR)
-        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_LINEAR>), gd, bd, 0, s, a);
+        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_LINEAR, false>), gd, bd, 0, s, a);
     else if (fmt == MXQ_MXFP8)
-        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_SWIZZLED>), gd, bd, 0, s, a);
+        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_SWIZZLED, false>), gd, bd, 0, s, a);
+    else if (layout == MXQ_SF_LINEAR && !auto_scale)
+        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_LINEAR, false>), gd, bd, 0, s, a);
+    else if (!auto_scale)
+        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_SWIZZLED, false>), gd, bd, 0, s, a);
     else if (layout == MXQ_SF_LINEAR)
-        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_LINEAR>), gd, bd, 0, s, a);
+        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_LINEAR, true>), gd, bd, 0, s, a);
     else
-        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_SWIZZLED>), gd, bd, 0, s, a);
+        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_SWIZZLED, true>), gd, bd, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax(const GroupArgs &a, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_slots, dim3(1), dim3(64), 0, s, a.amax_bits, a.n_slots);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || a.total_units == 0) return err;
+    const int64_t runs = (a.total_units + kAmaxUnits - 1) / kAmaxUnits;
+    hipLaunchKernelGGL(k_amax, dim3(grid_of(grid < runs ? grid : runs)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

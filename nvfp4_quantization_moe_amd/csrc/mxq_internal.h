@@ -28,6 +28,8 @@ struct GEntry {
     int64_t ld;           // row stride, elements
     int32_t rows;
     int32_t unit_begin;   // index of this entry's first work unit
+    int32_t slot;         // encode-scale slot (scales from the data)
+    int32_t pad_;
 };
 
 struct GroupArgs {
@@ -38,6 +40,11 @@ struct GroupArgs {
     int32_t sf_stride;    // swizzled: round_up(C, 4); linear: C
     int32_t n_cc;         // 512-column chunks per row
     int32_t total_units;
+    // encode scales from the data: per-slot amax as fp32 bits (zeroed, then
+    // reduced by k_amax) and the encode scales written by the quantize pass
+    uint32_t *amax_bits;
+    float *g_out;
+    int32_t n_slots;
 };
 
 constexpr int kMaxSplitsPerLaunch = 256;
@@ -87,7 +94,10 @@ struct SwizzleArgs {
 };
 
 // Launchers: return hipSuccess or the launch error.
-hipError_t launch_grouped(int fmt, int layout, const GroupArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_grouped(int fmt, int layout, bool auto_scale, const GroupArgs &a, int64_t grid,
+                          hipStream_t s);
+// Zero a.amax_bits[0..n_slots), then reduce each slot's amax into it.
+hipError_t launch_amax(const GroupArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,
                         hipStream_t s);
 hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s);

@@ -20,15 +20,6 @@
 
 namespace mxq {
 
-// Row-scaled NVFP4 encode scale of a row with amax a: 1 for an all-zero row,
-// else fp32(2688 / a) (IEEE division; 2688 = 448 * 6 maps the row amax onto
-// the largest block scale times the largest element) clamped to
-// [2^-100, 2^100], the range in which nv_scale's multipliers are exact.
-__device__ __forceinline__ float nv_row_encode_scale(float a) {
-    if (a == 0.0f) return 1.0f;
-    return __builtin_fminf(__builtin_fmaxf(2688.0f / a, 0x1p-100f), 0x1p100f);
-}
-
 // Up to 8 half-row steps fit in 128 VGPRs, so two workgroups share a CU;
 // wider rows get the whole register file.
 template <int FMT, bool ROWSC, int LAYOUT, int NCH2>
@@ -156,7 +147,7 @@ void k_split(const SplitArgs a) {
                 if (j < n_live) {
                     const uint32_t ra = max(half_max[it & 1][2 * pair], half_max[it & 1][2 * pair + 1]);
                     const float af = __uint_as_float(ra << 16);
-                    const float gr = nv_row_encode_scale(af);
+                    const float gr = nv_encode_scale(af);
                     uint32_t unused = 0;
                     const int r = encode(j, gr, nv_wave_quot(gr), unused);
                     if (a.row_amax && half == 0 && lane == 0) a.row_amax[e0 + r] = af;

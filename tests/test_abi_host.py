@@ -204,3 +204,27 @@ def test_binding_refuses_cpu_tensors():
         mxq.mx_quant_grouped(mxq.MXFP8, mxq.LINEAR, [x])
     with pytest.raises(ValueError):
         mxq.scale_swizzle(torch.zeros(4, 4, dtype=torch.uint8))
+
+
+def _auto(ents, slots=None, n_slots=None, g=A, am=A, layout=1, cols=64):
+    n = len(ents)
+    arr = (_Entry * max(n, 1))(*ents)
+    sl = None if slots is None else (ctypes.c_int * len(slots))(*slots)
+    ns = n if n_slots is None else n_slots
+    return mxq.lib().nvfp4_quant_grouped_auto(layout, cols, arr, n, sl, ns, g, am, None)
+
+
+def test_grouped_auto_validation():
+    e = _ent(g=0)  # entries' own global_scale is not used
+    assert _auto([e], n_slots=0) == EINVAL
+    assert _auto([e] * 2, n_slots=17, slots=[0, 0]) == EINVAL
+    assert _auto([e] * 3, n_slots=2) == EINVAL             # no slot map: one slot per entry
+    assert _auto([e] * 2, slots=[0, 2], n_slots=2) == EINVAL  # slot out of range
+    assert _auto([e] * 2, slots=[0, -1], n_slots=2) == EINVAL
+    assert _auto([e], g=0) == EINVAL
+    assert _auto([e], am=0) == EINVAL
+    assert _auto([e], g=A + 2) == ESHAPE
+    assert _auto([e], am=A + 1) == ESHAPE
+    assert _auto([e], cols=40) == ESHAPE                   # 40 % 16
+    assert _auto([e] * 17, n_slots=16, slots=[0] * 17) == EINVAL
+    assert _auto([_ent(src=0)]) == EINVAL
