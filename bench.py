@@ -25,16 +25,16 @@ import time
 
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3_235b_layer.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "nvfp4_quantization_moe_amd", "csrc")
 
 
-def kernel_source_hash():
+def source_hash(files):
     import hashlib
-    d = os.path.join(ROOT, "nvfp4_quantization_moe_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
+    for f in files:
         h.update(f.encode())
-        with open(os.path.join(d, f), "rb") as fh:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -42,16 +42,16 @@ def kernel_source_hash():
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated on a device copy), or None
-    when the kernel sources changed since the counters were taken."""
+    when a source the kernel is built from changed since the counters were
+    taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            k = json.load(f)["kernels"][kernel]
+        if k["source_sha256"] != source_hash(k["sources"]):
+            return None
+        return k["traffic_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
         return None
-    if t.get("source_sha256") != kernel_source_hash():
-        return None
-    k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k["traffic_bytes_per_launch"]
 
 
 def log(*a):
