@@ -14,7 +14,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/mxq.h"
+#include "mxq.h"
 
 namespace mxq {
 

@@ -1,8 +1,8 @@
 // mxq_fused.hip -- the fused residual add + RMSNorm + quantize epilogue, and
 // the linear -> swizzled scale conversion.
 //
-// The epilogue needs whole rows (the RMSNorm sum of squares): two waves own
-// one row and hold it in registers; a unit is 4 rows.  Swizzled units take
+// The epilogue needs whole rows (the RMSNorm sum of squares): two or four
+// waves own one row and hold it in registers; a unit is 4 rows.  Swizzled units take
 // rows band*128 + 32*q + gi (gi = 0..31), so a unit writes one 16-byte piece
 // of each tile line (8 consecutive units complete it).  Unit u runs on
 // workgroup u in plain dispatch order; every byte has one writer.
@@ -12,11 +12,12 @@
 namespace mxq {
 
 // ---------------------------------------------------------------------------
-// Whole-row units: 4 rows per workgroup of 8 waves, two waves per row; each
-// wave holds half of its row in registers (512-column steps 2k + half).  The
-// sum of squares combines the two halves through LDS in a fixed order.
-// Staged scales: swizzled [tile][row][4] (16 bytes per tile), linear [row][C].
+// A unit is 4 rows; WPR waves share each row, wave `part` holding the
+// 512-column steps WPR*k + part of it in registers.  gamma is staged in LDS
+// once per workgroup.  Staged scales: swizzled [tile][row][4] (16 bytes per
+// tile), linear [row][C].
 // ---------------------------------------------------------------------------
+
 template <int LAYOUT>
 __device__ __forceinline__ void stage_code(uint8_t *stage, int q, int c, int sf_cols,
                                            uint32_t code) {
@@ -33,66 +34,77 @@ __device__ __forceinline__ void stage_zero_row(uint8_t *stage, int q, int lane, 
     for (int c = lane; c < sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, sf_cols, 0);
 }
 
-// Copy n staged bytes to global memory with kRowThreads threads.
+// Copy n staged bytes to global memory with the whole workgroup (NT threads).
+template <int NT>
 __device__ __forceinline__ void copy_out_rows(uint8_t *dst, const uint8_t *src, int n) {
     if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
         const int nv = n >> 4;
-        for (int k = threadIdx.x; k < nv; k += kRowThreads)
+        for (int k = threadIdx.x; k < nv; k += NT)
             *reinterpret_cast<u32x4 *>(dst + k * 16) = *reinterpret_cast<const u32x4 *>(src + k * 16);
-        for (int k = (nv << 4) + threadIdx.x; k < n; k += kRowThreads) dst[k] = src[k];
+        for (int k = (nv << 4) + threadIdx.x; k < n; k += NT) dst[k] = src[k];
     } else {
-        for (int k = threadIdx.x; k < n; k += kRowThreads) dst[k] = src[k];
+        for (int k = threadIdx.x; k < n; k += NT) dst[k] = src[k];
     }
 }
 
-// Fused swizzled units take rows band*128 + 32*q + gi (gi = lu mod 32): one
+// Swizzled units take rows band*128 + 32*q + gi (gi = lu mod 32): one
 // 16-byte piece per tile line.
+template <int NT>
 __device__ __forceinline__ void flush_interleaved_swz(const uint8_t *stage, uint8_t *region,
                                                       int lu, int sf_stride) {
     const int tiles = sf_stride >> 2;
     uint8_t *base = region + (int64_t)(lu >> 5) * tiles * 512 + (lu & 31) * 16;
-    for (int t = threadIdx.x; t < tiles; t += kRowThreads)
+    for (int t = threadIdx.x; t < tiles; t += NT)
         *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512) =
             *reinterpret_cast<const u32x4 *>(stage + t * 16);
 }
 
 // Fused residual add + RMSNorm + quantize.  The row's bf16 residual sum stays
-// in registers; the sum of squares is each wave's fixed-order partial,
-// combined lower half + upper half; norm_out and the quantized form come
-// from the same bf16 values.
-template <int FMT, int LAYOUT, int NCH2>
-__global__ __launch_bounds__(kRowThreads) void k_fused(const FusedArgs a) {
+// in registers; the sum of squares is each wave's fixed-order partial, the
+// row's WPR partials added in wave order; norm_out and the quantized form come
+// from the same bf16 values.  NCHW: 512-column steps per wave.  With two waves
+// per row the kernel is held to 128 VGPRs, so two workgroups share a CU.
+template <int FMT, int LAYOUT, int NCHW, int WPR>
+__global__ __launch_bounds__(kRowUnit * WPR * kWave)
+__attribute__((amdgpu_waves_per_eu(WPR == 2 ? 4 : 1)))
+void k_fused(const FusedArgs a) {
     using Tr = FmtTraits<FMT>;
-    extern __shared__ __align__(16) uint8_t stage[];
-    __shared__ float red[8];
+    constexpr int kNT = kRowUnit * WPR * kWave;
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ float red[kRowUnit * WPR];
+    const int H = a.H;
+    uint16_t *gamma_s = reinterpret_cast<uint16_t *>(smem);
+    uint8_t *stage = smem + ((2 * H + 15) & ~15);
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
-    const int q = w >> 1, half = w & 1;
-    const int H = a.H;
+    const int q = w / WPR, part = w % WPR;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
     const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
     const float quot = FMT == MXQ_NVFP4 ? nv_wave_quot(g) : 0.0f;
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
+    for (int k = threadIdx.x * 8; k < H; k += kNT * 8)  // H is a multiple of 16
+        *reinterpret_cast<u32x4 *>(gamma_s + k) = *reinterpret_cast<const u32x4 *>(a.gamma + k);
+    __syncthreads();
     for (int lu = blockIdx.x; lu < a.total_units; lu += gridDim.x) {
         const int r = LAYOUT == MXQ_SF_SWIZZLED ? (lu >> 5) * 128 + 32 * q + (lu & 31)
                                                 : lu * 4 + q;
         const bool live = r < a.T;
         const int64_t rb = (int64_t)r * H;
-        u32x4 xv[NCH2];
+        u32x4 xv[NCHW];
         float acc = 0.0f;
         if (live) {
-            u32x4 rv[NCH2];
+            u32x4 rv[NCHW];
 #pragma unroll
-            for (int k = 0; k < NCH2; ++k) {
-                const int col = (2 * k + half) * kChunk + lane * 8;
+            for (int k = 0; k < NCHW; ++k) {
+                const int col = (WPR * k + part) * kChunk + lane * 8;
                 if (col < H) {
                     xv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + rb + col));
                     rv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.res + rb + col));
                 }
             }
 #pragma unroll
-            for (int k = 0; k < NCH2; ++k) {
-                const int col = (2 * k + half) * kChunk + lane * 8;
+            for (int k = 0; k < NCHW; ++k) {
+                const int col = (WPR * k + part) * kChunk + lane * 8;
                 if (col < H) {
                     u32x4 sum;
 #pragma unroll
@@ -114,22 +126,20 @@ __global__ __launch_bounds__(kRowThreads) void k_fused(const FusedArgs a) {
         if (lane == 0) red[w] = acc;
         __syncthreads();
         if (live) {
-            const float inv = 1.0f / __builtin_sqrtf((red[2 * q] + red[2 * q + 1]) / (float)H + a.eps);
-            u32x4 gm[NCH2];
+            float ss = red[q * WPR];
 #pragma unroll
-            for (int k = 0; k < NCH2; ++k) {
-                const int col = (2 * k + half) * kChunk + lane * 8;
-                if (col < H) gm[k] = *reinterpret_cast<const u32x4 *>(a.gamma + col);
-            }
+            for (int p = 1; p < WPR; ++p) ss += red[q * WPR + p];
+            const float inv = 1.0f / __builtin_sqrtf(ss / (float)H + a.eps);
 #pragma unroll
-            for (int k = 0; k < NCH2; ++k) {
-                const int col = (2 * k + half) * kChunk + lane * 8;
+            for (int k = 0; k < NCHW; ++k) {
+                const int col = (WPR * k + part) * kChunk + lane * 8;
                 u32x4 nv = u32x4{0, 0, 0, 0};
                 if (col < H) {
+                    const u32x4 gm = *reinterpret_cast<const u32x4 *>(gamma_s + col);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float nlo = (bf16_lo(xv[k][j]) * bf16_lo(gm[k][j])) * inv;
-                        const float nhi = (bf16_hi(xv[k][j]) * bf16_hi(gm[k][j])) * inv;
+                        const float nlo = (bf16_lo(xv[k][j]) * bf16_lo(gm[j])) * inv;
+                        const float nhi = (bf16_hi(xv[k][j]) * bf16_hi(gm[j])) * inv;
                         nv[j] = pack_bf16(nlo, nhi);
                     }
                     __builtin_nontemporal_store(nv, reinterpret_cast<u32x4 *>(a.norm_out + rb + col));
@@ -141,14 +151,14 @@ __global__ __launch_bounds__(kRowThreads) void k_fused(const FusedArgs a) {
                     if (leader) stage_code<LAYOUT>(stage, q, col / Tr::kBlock, a.sf_cols, code);
                 }
             }
-        } else if (LAYOUT == MXQ_SF_SWIZZLED && half == 0) {
+        } else if (LAYOUT == MXQ_SF_SWIZZLED && part == 0) {
             stage_zero_row<LAYOUT>(stage, q, lane, a.sf_cols, a.sf_stride);
         }
         __syncthreads();
         if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-            flush_interleaved_swz(stage, a.scales, lu, a.sf_stride);
+            flush_interleaved_swz<kNT>(stage, a.scales, lu, a.sf_stride);
         else
-            copy_out_rows(a.scales + (int64_t)lu * 4 * a.sf_cols, stage,
+            copy_out_rows<kNT>(a.scales + (int64_t)lu * 4 * a.sf_cols, stage,
                           min(4, a.T - lu * 4) * a.sf_cols);
         __syncthreads();
     }
@@ -186,30 +196,49 @@ __global__ __launch_bounds__(kThreads) void k_swizzle(const SwizzleArgs a) {
 // ---------------------------------------------------------------------------
 static inline unsigned grid_of(int64_t g) { return (unsigned)(g < 1 ? 1 : g); }
 
-template <int FMT, int LAYOUT>
+// 512-column steps per wave for a row of H columns shared by wpr waves,
+// rounded up to an instantiated count.
+static int fused_steps(int64_t H, int wpr) {
+    const int64_t n = ((H + kChunk - 1) / kChunk + wpr - 1) / wpr;
+    return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 7 ? 7 : n <= 8 ? 8 : 16;
+}
+
+template <int FMT, int LAYOUT, int WPR>
 static void fused_nch(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
-    const dim3 bd(kRowThreads);
-    switch (half_row_steps(a.H)) {
-    case 1: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 1>), gd, bd, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 2>), gd, bd, lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 4>), gd, bd, lds, s, a); break;
-    case 7: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 7>), gd, bd, lds, s, a); break;
-    case 8: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 8>), gd, bd, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16>), gd, bd, lds, s, a); break;
+    const dim3 bd(kRowUnit * WPR * kWave);
+    switch (fused_steps(a.H, WPR)) {
+    case 1: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 1, WPR>), gd, bd, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 2, WPR>), gd, bd, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 4, WPR>), gd, bd, lds, s, a); break;
+    case 7: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 7, WPR>), gd, bd, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 8, WPR>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16, WPR>), gd, bd, lds, s, a); break;
     }
 }
 
+// Up to 2048 rows, four waves per row (shorter per-row chains: latency bound);
+// beyond, two waves per row in half the threads (more workgroups per CU:
+// bandwidth bound).  Measured on H = 7168.
+template <int FMT, int LAYOUT>
+static void fused_wpr(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
+    if (a.T <= 2048)
+        fused_nch<FMT, LAYOUT, 4>(a, gd, lds, s);
+    else
+        fused_nch<FMT, LAYOUT, 2>(a, gd, lds, s);
+}
+
 hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s) {
-    const size_t lds = (size_t)4 * a.sf_stride;
+    // gamma (bf16 [H], 16-byte rounded) then the staged scales of 4 rows
+    const size_t lds = (size_t)((2 * a.H + 15) & ~15) + (size_t)4 * a.sf_stride;
     const dim3 gd(grid_of(grid));
     if (fmt == MXQ_MXFP8 && layout == MXQ_SF_LINEAR)
-        fused_nch<MXQ_MXFP8, MXQ_SF_LINEAR>(a, gd, lds, s);
+        fused_wpr<MXQ_MXFP8, MXQ_SF_LINEAR>(a, gd, lds, s);
     else if (fmt == MXQ_MXFP8)
-        fused_nch<MXQ_MXFP8, MXQ_SF_SWIZZLED>(a, gd, lds, s);
+        fused_wpr<MXQ_MXFP8, MXQ_SF_SWIZZLED>(a, gd, lds, s);
     else if (layout == MXQ_SF_LINEAR)
-        fused_nch<MXQ_NVFP4, MXQ_SF_LINEAR>(a, gd, lds, s);
+        fused_wpr<MXQ_NVFP4, MXQ_SF_LINEAR>(a, gd, lds, s);
     else
-        fused_nch<MXQ_NVFP4, MXQ_SF_SWIZZLED>(a, gd, lds, s);
+        fused_wpr<MXQ_NVFP4, MXQ_SF_SWIZZLED>(a, gd, lds, s);
     return hipGetLastError();
 }
 

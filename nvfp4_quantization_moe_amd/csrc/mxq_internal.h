@@ -6,7 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/mxq.h"
+#include "mxq.h"
 
 namespace mxq {
 
@@ -15,7 +15,6 @@ constexpr int kRowsPerWave = 4;                // rows per wave in a grouped uni
 constexpr int kUnitRows = 4 * kRowsPerWave;   // rows per grouped work unit
 constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
 constexpr int kRowUnit = 4;    // rows per split/fused work unit
-constexpr int kRowThreads = 512;  // fused workgroup: 8 waves, 2 per row
 constexpr int kSplitThreads = 512;  // split workgroup: 8 waves, 2 per row
 
 // One grouped-launch descriptor.  The whole table travels in the kernel

@@ -173,3 +173,44 @@ def test_swizzle_of_linear_equals_swizzled_quant(orc):
     conv = mxq.scale_swizzle(s_lin[0].view(300, 128))
     torch.cuda.synchronize()
     assert torch.equal(conv, s_swz[0])
+
+
+def _fused_check(orc, T, H, fmt, layout, seed, eps=1e-6, g=37.5):
+    x_c, r_c, g_c = workloads.epilogue_inputs(T, H, seed=seed)
+    x, r, gm = x_c.to(DEV), r_c.to(DEV), g_c.to(DEV)
+    gs = torch.tensor([g], dtype=torch.float32, device=DEV)
+    pw = H if fmt == mxq.MXFP8 else H // 2
+    nb = mxq.scale_bytes(T, H, fmt, layout)
+    pay, pwh = canary_buffer(T * pw)
+    sc, swh = canary_buffer(nb)
+    ro, no = torch.empty_like(x), torch.empty_like(x)
+    mxq.rmsnorm_quant_fused(x, r, gm, eps, fmt, layout, gs, out=(ro, no, pay.view(T, pw), sc))
+    torch.cuda.synchronize()
+    assert guard_intact(pwh, T * pw) and guard_intact(swh, nb)
+    oro, ono = orc.add_rmsnorm(bf16_bits(x_c), bf16_bits(r_c), bf16_bits(g_c), eps)
+    assert np.array_equal(bf16_bits(ro), oro)
+    assert bf16_ulp_diff(bf16_bits(no), ono).max() <= 1
+    qp, qs = orc.quantize(fmt, layout, bf16_bits(no), g=g)
+    assert np.array_equal(u8(pay), qp.ravel()) and np.array_equal(u8(sc), qs)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_fused_widths_both_row_splits(orc, fmt, layout):
+    """Row widths with ragged 512-column tails, up to the 16384 maximum, on
+    both sides of the launcher's switch from four to two waves per row."""
+    for T, H in ((5, 128), (5, 640), (3, 16384), (130, 2176), (2100, 640), (2049, 2176)):
+        say("fused widths, fmt", fmt, "layout", layout, "T", T, "H", H)
+        _fused_check(orc, T, H, fmt, layout, seed=T + H)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_fused_grid_invariance(orc, fmt):
+    try:
+        for T in (100, 2100):
+            for cap in (1, 7):
+                mxq.set_max_workgroups(cap)
+                say("fused grid cap", cap, "T", T, "fmt", fmt)
+                _fused_check(orc, T, 1024, fmt, mxq.SWIZZLED, seed=T)
+    finally:
+        mxq.set_max_workgroups(0)
