@@ -189,6 +189,25 @@ int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, i
     const int64_t C = cols / block_of(fmt);
     const int64_t Cs = layout == MXQ_SF_SWIZZLED ? round_up(C, 4) : C;
     const int64_t payload_ld = fmt == MXQ_MXFP8 ? cols : cols / 2;
+    // Linear scales need no per-expert padding: expert i's region starts at
+    // o_i * C and its local row r - o_i sits at r * C, so the bulk buffer is
+    // the [total_rows, C] scale matrix of the whole activation and the split
+    // is one tensor's quantization (units then span expert boundaries).
+    const int64_t whole[1] = {total_rows};
+    if (layout == MXQ_SF_LINEAR) {
+        split_rows = whole;
+        n_splits = 1;
+    }
+    // Units of 8 rows keep more workgroups in flight; with swizzled scales
+    // and short experts (under 128 rows on average, so most 128-row bands are
+    // mostly padding) units of whole 128-byte tile lines (32 rows) measured
+    // faster.
+    int sub = 2;
+    if (layout == MXQ_SF_SWIZZLED) {
+        int64_t nonempty = 0;
+        for (int i = 0; i < n_splits; ++i) nonempty += split_rows[i] > 0;
+        if (nonempty > 0 && total_rows < 128 * nonempty) sub = 8;
+    }
     int64_t row_base = 0, scale_base = 0;
     for (int first = 0; first < n_splits; first += kMaxSplitsPerLaunch) {
         const int n = n_splits - first < kMaxSplitsPerLaunch ? n_splits - first
@@ -204,14 +223,17 @@ int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, i
         a.sf_cols = (int32_t)C;
         a.sf_stride = (int32_t)Cs;
         a.n = n;
+        a.sub = sub;
         int64_t rows = 0, units = 0, sbytes = 0;
         for (int j = 0; j < n; ++j) {
             const int64_t m = split_rows[first + j];
             a.row_off[j] = (int32_t)rows;
             a.unit_off[j] = (int32_t)units;
             rows += m;
-            // swizzled: 4 line-sets per 128-row band; linear: 32-row groups
-            units += layout == MXQ_SF_SWIZZLED ? (m + 127) / 128 * 4 : (m + 31) / 32;
+            // swizzled: 32 / sub line segments per 128-row band; linear:
+            // groups of 4 * sub rows
+            units += layout == MXQ_SF_SWIZZLED ? (m + 127) / 128 * (32 / sub)
+                                               : (m + 4 * sub - 1) / (4 * sub);
             sbytes += sf_bytes(m, C, layout);
         }
         a.row_off[n] = (int32_t)rows;

@@ -49,8 +49,9 @@ struct GroupArgs {
 constexpr int kMaxSplitsPerLaunch = 256;
 
 // Up to 256 consecutive splits of a concatenated activation.  A work unit is
-// 32 rows of one expert (swizzled: the rows of one 128-row band that share
-// line h of every scale tile); units never straddle two experts.
+// 4*sub rows of one expert (swizzled: the rows of one 128-row band that share
+// a sub-row segment of line h of every scale tile); units never straddle two
+// experts.
 struct SplitArgs {
     const uint16_t *src;  // global row 0 of this launch's first split
     uint8_t *payload;     // same row
@@ -62,6 +63,7 @@ struct SplitArgs {
     int32_t sf_stride;
     int32_t n;            // splits in this launch
     int32_t total_units;
+    int32_t sub;          // rows per tile-line segment: 2 or 8 (linear: 2)
     int32_t row_off[kMaxSplitsPerLaunch + 1];   // prefix sums of split rows
     int32_t unit_off[kMaxSplitsPerLaunch + 1];  // prefix sums of split units
 };

@@ -5,10 +5,13 @@
 // scale, row-scaled NVFP4 (each row under an encode scale derived from its own
 // amax) and MXFP8.
 //
-// Swizzled: a unit owns line h (0..3) of every scale tile of one 128-row band
-// of one expert, i.e. the rows band*128 + 32*q + 8*h + i (q < 4, i < 8), so
-// its staged scales leave as whole 128-byte lines, padding rows and columns
-// zero.  Linear: a unit is 32 consecutive rows.  Only the unit's live rows are
+// Swizzled: a unit owns the SUB-row segment `sub` of line h (0..3) of every
+// scale tile of one 128-row band of one expert, i.e. the rows
+// band*128 + 32*q + 8*h + SUB*sub + i (q < 4, i < SUB), so its staged scales
+// leave as whole 16*SUB-byte segments, padding rows and columns zero.
+// Linear: a unit is 4*SUB consecutive rows.  SUB is 8 (whole 128-byte lines:
+// fewer, fuller units when experts are short) or 2 (more workgroups in
+// flight); the host picks it per call.  Only the unit's live rows are
 // loaded: pairs of waves take them in turn, each wave holding half of a row
 // (512-column steps 2k + half) in registers, so short experts keep every wave
 // busy.  A wave loads its next row only after storing the current one:
@@ -22,12 +25,13 @@ namespace mxq {
 
 // Up to 8 half-row steps fit in 128 VGPRs, so two workgroups share a CU;
 // wider rows get the whole register file.
-template <int FMT, bool ROWSC, int LAYOUT, int NCH2>
+template <int FMT, bool ROWSC, int LAYOUT, int NCH2, int SUB>
 __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(NCH2 <= 8 ? 4 : 1)))
 void k_split(const SplitArgs a) {
     using Tr = FmtTraits<FMT>;
+    constexpr int kUnit = 4 * SUB;  // rows per unit
     extern __shared__ __align__(16) uint8_t stage[];
-    __shared__ uint32_t row_max[32];     // one encode scale: row amax folded by LDS atomics
+    __shared__ uint32_t row_max[kUnit];  // one encode scale: row amax folded by LDS atomics
     __shared__ uint32_t half_max[2][8];  // row-scaled: each wave's half-row amax, two buffers
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
@@ -36,7 +40,7 @@ void k_split(const SplitArgs a) {
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
     const float g = (FMT == MXQ_NVFP4 && !ROWSC) ? *a.g : 0.0f;
     const float quot = (FMT == MXQ_NVFP4 && !ROWSC) ? nv_wave_quot(g) : 0.0f;
-    const int stage_bytes = 32 * a.sf_stride;
+    const int stage_bytes = kUnit * a.sf_stride;
     int it = 0;  // row-scaled step counter, uniform over the workgroup
     for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
         int lo = 0, hi = a.n;  // split s with unit_off[s] <= u < unit_off[s + 1]
@@ -49,21 +53,24 @@ void k_split(const SplitArgs a) {
         const int m = a.row_off[s + 1] - a.row_off[s];
         const int64_t e0 = a.row_off[s];  // expert's first row
         // live rows of the unit, in order; nq[q] of them in line-set row q
+        constexpr int kSeg = SUB * 16;  // bytes of each tile the unit fills
         int nq[4] = {0, 0, 0, 0};
         int n_live;
-        int band = 0, h = 0;
+        int band = 0, h = 0, sub = 0;
         if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-            band = lu >> 2;
-            h = lu & 3;
+            constexpr int kPerBand = 32 / SUB;
+            band = lu / kPerBand;
+            h = (lu % kPerBand) / (8 / SUB);
+            sub = lu % (8 / SUB);
             const int rb = min(128, m - band * 128);
             n_live = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                nq[q] = min(8, max(0, rb - 32 * q - 8 * h));
+                nq[q] = min(SUB, max(0, rb - 32 * q - 8 * h - SUB * sub));
                 n_live += nq[q];
             }
         } else {
-            n_live = min(32, m - lu * 32);
+            n_live = min(kUnit, m - lu * kUnit);
         }
         // j-th live row of the unit -> (line-set row q, slot i, row in expert)
         auto locate = [&](int j, int &q, int &i) {
@@ -71,9 +78,9 @@ void k_split(const SplitArgs a) {
             i = j;
             if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
                 while (i >= nq[q]) { i -= nq[q]; ++q; }
-                return band * 128 + 32 * q + 8 * h + i;
+                return band * 128 + 32 * q + 8 * h + SUB * sub + i;
             } else {
-                return lu * 32 + j;
+                return lu * kUnit + j;
             }
         };
         auto load_row = [&](int j, u32x4 *v) {
@@ -112,7 +119,7 @@ void k_split(const SplitArgs a) {
                     if (leader) {
                         const int c = col / Tr::kBlock;
                         if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-                            stage[(c >> 2) * 128 + i * 16 + q * 4 + (c & 3)] = (uint8_t)code;
+                            stage[(c >> 2) * kSeg + i * 16 + q * 4 + (c & 3)] = (uint8_t)code;
                         else
                             stage[j * a.sf_cols + c] = (uint8_t)code;
                     }
@@ -126,7 +133,7 @@ void k_split(const SplitArgs a) {
             for (int k = threadIdx.x * 16; k < stage_bytes; k += kSplitThreads * 16)
                 *reinterpret_cast<u32x4 *>(stage + k) = u32x4{0, 0, 0, 0};
         }
-        if (!ROWSC && threadIdx.x < 32) row_max[threadIdx.x] = 0;
+        if (!ROWSC && threadIdx.x < kUnit) row_max[threadIdx.x] = 0;
         __syncthreads();
         if constexpr (!ROWSC) {
             for (int j = pair; j < n_live; j += 4) {
@@ -163,15 +170,15 @@ void k_split(const SplitArgs a) {
         }
         if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
             const int tiles = a.sf_stride >> 2;
-            uint8_t *base = a.scales + (int64_t)(a.unit_off[s] >> 2) * tiles * 512 +
-                            (int64_t)band * tiles * 512 + h * 128;
-            for (int k = threadIdx.x; k < tiles * 8; k += kSplitThreads) {
-                const int t = k >> 3, part = k & 7;
+            const int64_t first_band = a.unit_off[s] / (32 / SUB);
+            uint8_t *base = a.scales + (first_band + band) * tiles * 512 + h * 128 + sub * kSeg;
+            for (int k = threadIdx.x; k < tiles * SUB; k += kSplitThreads) {
+                const int t = k / SUB, part = k % SUB;
                 *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512 + part * 16) =
-                    *reinterpret_cast<const u32x4 *>(stage + t * 128 + part * 16);
+                    *reinterpret_cast<const u32x4 *>(stage + t * kSeg + part * 16);
             }
         } else {
-            uint8_t *dst = a.scales + (e0 + lu * 32) * a.sf_cols;
+            uint8_t *dst = a.scales + (e0 + lu * kUnit) * a.sf_cols;
             const int nbytes = n_live * a.sf_cols;
             if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
                 for (int k = threadIdx.x; k < (nbytes >> 4); k += kSplitThreads)
@@ -190,30 +197,32 @@ void k_split(const SplitArgs a) {
 // ---------------------------------------------------------------------------
 // Launcher.
 // ---------------------------------------------------------------------------
-template <int FMT, bool ROWSC, int LAYOUT>
+template <int FMT, bool ROWSC, int LAYOUT, int SUB>
 static void split_nch(const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
     const dim3 bd(kSplitThreads);
     switch (half_row_steps(a.cols)) {
-    case 1: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 1>), gd, bd, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 2>), gd, bd, lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 4>), gd, bd, lds, s, a); break;
-    case 7: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 7>), gd, bd, lds, s, a); break;
-    case 8: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 8>), gd, bd, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 16>), gd, bd, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 1, SUB>), gd, bd, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 2, SUB>), gd, bd, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 4, SUB>), gd, bd, lds, s, a); break;
+    case 7: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 7, SUB>), gd, bd, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 8, SUB>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 16, SUB>), gd, bd, lds, s, a); break;
     }
 }
 
 template <int FMT, bool ROWSC>
 static void split_layout(int layout, const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
     if (layout == MXQ_SF_LINEAR)
-        split_nch<FMT, ROWSC, MXQ_SF_LINEAR>(a, gd, lds, s);
+        split_nch<FMT, ROWSC, MXQ_SF_LINEAR, 2>(a, gd, lds, s);
+    else if (a.sub == 2)
+        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED, 2>(a, gd, lds, s);
     else
-        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED>(a, gd, lds, s);
+        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED, 8>(a, gd, lds, s);
 }
 
 hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,
                         hipStream_t s) {
-    const size_t lds = (size_t)32 * a.sf_stride;
+    const size_t lds = (size_t)4 * a.sub * a.sf_stride;
     const dim3 gd((unsigned)(grid < 1 ? 1 : grid));
     if (fmt == MXQ_MXFP8)
         split_layout<MXQ_MXFP8, false>(layout, a, gd, lds, s);

@@ -159,3 +159,34 @@ def test_split_many_launches(orc):
         for layout in (0, 1):
             say("600 splits, fmt", fmt, "layout", layout)
             check(orc, fmt, x_cpu, split, layout)
+
+
+LONG_SPLITS = ([0, 300, 129, 0, 500], [128, 256, 1], [1000], [128, 128])
+
+
+@pytest.mark.parametrize("mode", ["nvfp4", "nvfp4_row_scaled", "mxfp8"])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_split_long_experts(orc, mode, layout):
+    """Experts of 128 rows or more on average take the 8-row units (the
+    short-expert sets above take whole tile lines): same bytes as the oracle,
+    also with capped grids."""
+    fmt = mxq.MXFP8 if mode == "mxfp8" else mxq.NVFP4
+    for k, split in enumerate(LONG_SPLITS):
+        T, H = sum(split), 1536
+        x_cpu = extreme_rows(T, H, seed=40 + k)
+        x = x_cpu.to(DEV)
+        for cap in (0, 3):
+            mxq.set_max_workgroups(cap)
+            try:
+                say("long experts", mode, "layout", layout, "split", split, "cap", cap)
+                if mode == "nvfp4":
+                    g = torch.tensor([37.0], dtype=torch.float32, device=DEV)
+                    p, s, a = mxq.nvfp4_quant_split(x, split, g, layout)
+                    torch.cuda.synchronize()
+                    op, os_, oa = orc.split(fmt, bf16_bits(x_cpu), split, g=37.0, layout=layout)
+                    assert np.array_equal(u8(p), op.ravel()) and np.array_equal(u8(s), os_)
+                    assert np.array_equal(a.cpu().numpy(), oa)
+                else:
+                    check(orc, fmt, x_cpu, split, layout)
+            finally:
+                mxq.set_max_workgroups(0)
