@@ -294,7 +294,9 @@ def timed(torch, fn, iters, warm=3):
 
 
 def extra_workloads(torch, mxq, workloads, dev):
+    import ctypes
     res = {}
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     # attainable-bandwidth reference: a 4 GiB device copy (read + write)
     n = 1 << 31
     a = torch.empty(n, dtype=torch.bfloat16, device=dev)
@@ -367,13 +369,9 @@ def extra_workloads(torch, mxq, workloads, dev):
         for layout, lname in ((0, "linear"), (1, "swizzled")):
             total = mxq.split_scale_offset(split, len(split), H, fmt, layout)
             sc = torch.empty(total, dtype=torch.uint8, device=dev)
-            if mode == "nvfp4":
-                fn = lambda i: mxq.nvfp4_quant_split(xs[i % 8], split, g, layout, pay, sc, am)
-            elif mode == "nvfp4_row_scaled":
-                fn = lambda i: mxq.nvfp4_quant_split_row_scaled(xs[i % 8], split, layout, pay, sc, am)
-            else:
-                fn = lambda i: mxq.mxfp8_quant_split(xs[i % 8], split, layout, pay, sc, am)
-            t = timed(torch, fn, 20)
+            scs = [mxq.SplitCall(mode, xs[k], split, layout, g if mode == "nvfp4" else None,
+                                 pay, sc, am) for k in range(8)]
+            t = timed(torch, lambda i: scs[i % 8](stream), 20)
             nb = T * H * 2 + pay.numel() + total + 4 * T + (4 if mode == "nvfp4" else 0)
             splits[f"{mode}_{lname}"] = {"us": round(t * 1e6, 1), "alg_bytes": nb,
                                          "GBps": round(nb / t / 1e9, 1)}
@@ -394,8 +392,8 @@ def extra_workloads(torch, mxq, workloads, dev):
                     torch.empty(T, pw, dtype=torch.uint8, device=dev),
                     torch.empty(nsc, dtype=torch.uint8, device=dev))
             gf = torch.ones(1, dtype=torch.float32, device=dev)
-            t = timed(torch, lambda i: mxq.rmsnorm_quant_fused(*ins[i % 4], 1e-6, fmt, 1,
-                                                                 global_scale=gf, out=outs), 50)
+            fcs = [mxq.FusedCall(*ins[k], 1e-6, fmt, 1, gf, outs) for k in range(4)]
+            t = timed(torch, lambda i: fcs[i % 4](stream), 50)
             nb = T * H * 8 + T * pw + nsc + 2 * H + (4 if fmt == 1 else 0)
             entry = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
             if fmt == 0:

@@ -292,25 +292,73 @@ def _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales):
     return payloads, scales
 
 
-def _split_outputs(fmt, src, split_rows, layout, payload, scales, row_amax, want_row_amax):
-    _need_gpu(src, "src", torch.bfloat16)
-    if src.dim() != 2 or not src.is_contiguous():
-        raise ValueError("src must be a contiguous [T, H] bf16 tensor")
-    T, H = src.shape
-    dev = src.device
-    if payload is None:
-        payload = torch.empty((T, H if fmt == MXFP8 else H // 2), dtype=torch.uint8, device=dev)
-    if scales is None:
+def _check_out(t, name, dtype, numel):
+    _need_gpu(t, name, dtype)
+    if not t.is_contiguous() or t.numel() < numel:
+        raise ValueError(f"{name}: needs a contiguous tensor of at least {numel} elements")
+
+
+SPLIT_MODES = ("nvfp4", "nvfp4_row_scaled", "mxfp8")
+
+
+class SplitCall:
+    """A split quantization with its arguments checked and packed once.
+
+    mode: "nvfp4" (one encode scale, global_scale required),
+    "nvfp4_row_scaled" (per-row encode scales) or "mxfp8".  Outputs are
+    allocated when None: payload [T, H] (MXFP8) or [T, H/2], the bulk scale
+    buffer (expert i at split_scale_offset(split_rows, i, H, fmt, layout)) and
+    row_amax [T] (always for row-scaled; otherwise when want_row_amax).
+    Calling returns (payload, scales, row_amax).  The tensors must stay alive."""
+
+    def __init__(self, mode, src, split_rows, layout=SWIZZLED, global_scale=None, payload=None,
+                 scales=None, row_amax=None, want_row_amax=True):
+        if mode not in SPLIT_MODES:
+            raise ValueError(f"mode must be one of {SPLIT_MODES}")
+        fmt = MXFP8 if mode == "mxfp8" else NVFP4
+        _need_gpu(src, "src", torch.bfloat16)
+        if src.dim() != 2 or not src.is_contiguous():
+            raise ValueError("src must be a contiguous [T, H] bf16 tensor")
+        T, H = src.shape
+        dev = src.device
+        split_rows = [int(v) for v in split_rows]
+        pw = H if fmt == MXFP8 else H // 2
         total = split_scale_offset(split_rows, len(split_rows), H, fmt, layout)
-        scales = torch.empty(total, dtype=torch.uint8, device=dev)
-    if row_amax is None and want_row_amax:
-        row_amax = torch.empty(T, dtype=torch.float32, device=dev)
-    _need_gpu(payload, "payload", torch.uint8)
-    _need_gpu(scales, "scales", torch.uint8)
-    if row_amax is not None:
-        _need_gpu(row_amax, "row_amax", torch.float32)
-    arr = (ctypes.c_int64 * max(len(split_rows), 1))(*split_rows)
-    return T, H, payload, scales, row_amax, arr
+        if payload is None:
+            payload = torch.empty((T, pw), dtype=torch.uint8, device=dev)
+        if scales is None:
+            scales = torch.empty(total, dtype=torch.uint8, device=dev)
+        if row_amax is None and (want_row_amax or mode == "nvfp4_row_scaled"):
+            row_amax = torch.empty(T, dtype=torch.float32, device=dev)
+        _check_out(payload, "payload", torch.uint8, T * pw)
+        _check_out(scales, "scales", torch.uint8, total)
+        if row_amax is not None:
+            _check_out(row_amax, "row_amax", torch.float32, T)
+        if mode == "nvfp4":
+            if global_scale is None:
+                raise ValueError("nvfp4 split needs global_scale")
+            _need_gpu(global_scale, "global_scale", torch.float32)
+        self.mode, self.device = mode, dev
+        self.src, self.global_scale = src, global_scale
+        self.payload, self.scales, self.row_amax = payload, scales, row_amax
+        arr = (ctypes.c_int64 * max(len(split_rows), 1))(*split_rows)
+        head = (src.data_ptr(), T, H, arr, len(split_rows))
+        if mode == "nvfp4":
+            self._fn, self._args = "nvfp4_quant_split", head + (
+                global_scale.data_ptr(), payload.data_ptr(), scales.data_ptr(),
+                _ptr(row_amax), layout)
+        elif mode == "nvfp4_row_scaled":
+            self._fn, self._args = "nvfp4_quant_split_row_scaled", head + (
+                payload.data_ptr(), scales.data_ptr(), row_amax.data_ptr(), layout)
+        else:
+            self._fn, self._args = "mxfp8_quant_split", head + (
+                payload.data_ptr(), scales.data_ptr(), _ptr(row_amax), layout)
+        self._arr = arr  # keep the split table alive
+
+    def __call__(self, stream: Optional[ctypes.c_void_p] = None):
+        stream = _stream(self.device) if stream is None else stream
+        _check(getattr(lib(), self._fn)(*self._args, stream), self._fn)
+        return self.payload, self.scales, self.row_amax
 
 
 def nvfp4_quant_split(src: torch.Tensor, split_rows: Sequence[int], global_scale: torch.Tensor,
@@ -320,15 +368,8 @@ def nvfp4_quant_split(src: torch.Tensor, split_rows: Sequence[int], global_scale
     """Quantize a concatenated bf16 activation [T, H] once and split it per
     expert.  Returns (payload [T, H/2], bulk scales, row_amax [T] or None);
     expert i's scales start at split_scale_offset(split_rows, i, H)."""
-    _need_gpu(global_scale, "global_scale", torch.float32)
-    split_rows = [int(v) for v in split_rows]
-    T, H, payload, scales, row_amax, arr = _split_outputs(
-        NVFP4, src, split_rows, layout, payload, scales, row_amax, want_row_amax)
-    rc = lib().nvfp4_quant_split(src.data_ptr(), T, H, arr, len(split_rows),
-                                 global_scale.data_ptr(), payload.data_ptr(), scales.data_ptr(),
-                                 _ptr(row_amax), layout, _stream(src.device))
-    _check(rc, "nvfp4_quant_split")
-    return payload, scales, row_amax
+    return SplitCall("nvfp4", src, split_rows, layout, global_scale, payload, scales, row_amax,
+                     want_row_amax)()
 
 
 def nvfp4_quant_split_row_scaled(src: torch.Tensor, split_rows: Sequence[int],
@@ -337,14 +378,8 @@ def nvfp4_quant_split_row_scaled(src: torch.Tensor, split_rows: Sequence[int],
                                  row_amax: Optional[torch.Tensor] = None):
     """Row-scaled NVFP4 split: row r under its own encode scale from its amax.
     Returns (payload [T, H/2], bulk scales, row_amax [T])."""
-    split_rows = [int(v) for v in split_rows]
-    T, H, payload, scales, row_amax, arr = _split_outputs(
-        NVFP4, src, split_rows, layout, payload, scales, row_amax, True)
-    rc = lib().nvfp4_quant_split_row_scaled(src.data_ptr(), T, H, arr, len(split_rows),
-                                            payload.data_ptr(), scales.data_ptr(),
-                                            row_amax.data_ptr(), layout, _stream(src.device))
-    _check(rc, "nvfp4_quant_split_row_scaled")
-    return payload, scales, row_amax
+    return SplitCall("nvfp4_row_scaled", src, split_rows, layout, None, payload, scales,
+                     row_amax)()
 
 
 def mxfp8_quant_split(src: torch.Tensor, split_rows: Sequence[int], layout: int = SWIZZLED,
@@ -353,13 +388,54 @@ def mxfp8_quant_split(src: torch.Tensor, split_rows: Sequence[int], layout: int 
                       row_amax: Optional[torch.Tensor] = None, want_row_amax: bool = True):
     """MXFP8 split.  Returns (payload [T, H], bulk scales, row_amax [T] or
     None); expert i's scales start at split_scale_offset(split_rows, i, H, MXFP8)."""
-    split_rows = [int(v) for v in split_rows]
-    T, H, payload, scales, row_amax, arr = _split_outputs(
-        MXFP8, src, split_rows, layout, payload, scales, row_amax, want_row_amax)
-    rc = lib().mxfp8_quant_split(src.data_ptr(), T, H, arr, len(split_rows), payload.data_ptr(),
-                                 scales.data_ptr(), _ptr(row_amax), layout, _stream(src.device))
-    _check(rc, "mxfp8_quant_split")
-    return payload, scales, row_amax
+    return SplitCall("mxfp8", src, split_rows, layout, None, payload, scales, row_amax,
+                     want_row_amax)()
+
+
+class FusedCall:
+    """rmsnorm_quant_fused with its arguments checked and packed once; calling
+    returns (residual_out, norm_out, payload, scales).  The tensors must stay
+    alive."""
+
+    def __init__(self, x, residual, gamma, eps=1e-6, fmt=MXFP8, layout=SWIZZLED,
+                 global_scale=None, out=None):
+        _need_gpu(x, "x", torch.bfloat16)
+        _need_gpu(residual, "residual", torch.bfloat16)
+        _need_gpu(gamma, "gamma", torch.bfloat16)
+        if x.dim() != 2 or not x.is_contiguous() or residual.shape != x.shape or \
+                not residual.is_contiguous() or gamma.shape != (x.shape[1],) or \
+                not gamma.is_contiguous():
+            raise ValueError("x, residual: contiguous [T, H]; gamma: contiguous [H]")
+        T, H = x.shape
+        dev = x.device
+        if fmt == NVFP4:
+            if global_scale is None:
+                raise ValueError("NVFP4 needs global_scale")
+            _need_gpu(global_scale, "global_scale", torch.float32)
+        pw = H if fmt == MXFP8 else H // 2
+        nb = lib().mxq_scale_bytes(T, H, fmt, layout)
+        if nb < 0:
+            raise ValueError("rmsnorm_quant_fused: bad H for this format")
+        if out is None:
+            out = (torch.empty_like(x), torch.empty_like(x),
+                   torch.empty((T, pw), dtype=torch.uint8, device=dev),
+                   torch.empty(nb, dtype=torch.uint8, device=dev))
+        res_out, norm_out, payload, scales = out
+        _check_out(res_out, "residual_out", torch.bfloat16, T * H)
+        _check_out(norm_out, "norm_out", torch.bfloat16, T * H)
+        _check_out(payload, "payload", torch.uint8, T * pw)
+        _check_out(scales, "scales", torch.uint8, nb)
+        self.device = dev
+        self.keep = (x, residual, gamma, global_scale)
+        self.out = (res_out, norm_out, payload, scales)
+        self._args = (fmt, layout, x.data_ptr(), residual.data_ptr(), gamma.data_ptr(),
+                      float(eps), T, H, _ptr(global_scale), res_out.data_ptr(),
+                      norm_out.data_ptr(), payload.data_ptr(), scales.data_ptr())
+
+    def __call__(self, stream: Optional[ctypes.c_void_p] = None):
+        stream = _stream(self.device) if stream is None else stream
+        _check(lib().rmsnorm_quant_fused(*self._args, stream), "rmsnorm_quant_fused")
+        return self.out
 
 
 def rmsnorm_quant_fused(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
@@ -368,33 +444,7 @@ def rmsnorm_quant_fused(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Te
     """residual_out = bf16(x + residual); norm_out = RMSNorm(residual_out) * gamma
     (bf16); payload/scales = fmt quantization of norm_out.  Returns
     (residual_out, norm_out, payload, scales)."""
-    _need_gpu(x, "x", torch.bfloat16)
-    _need_gpu(residual, "residual", torch.bfloat16)
-    _need_gpu(gamma, "gamma", torch.bfloat16)
-    if x.dim() != 2 or not x.is_contiguous() or residual.shape != x.shape or \
-            not residual.is_contiguous() or gamma.shape != (x.shape[1],) or not gamma.is_contiguous():
-        raise ValueError("x, residual: contiguous [T, H]; gamma: contiguous [H]")
-    T, H = x.shape
-    dev = x.device
-    if fmt == NVFP4:
-        if global_scale is None:
-            raise ValueError("NVFP4 needs global_scale")
-        _need_gpu(global_scale, "global_scale", torch.float32)
-    if out is None:
-        pw = H if fmt == MXFP8 else H // 2
-        nb = lib().mxq_scale_bytes(T, H, fmt, layout)
-        if nb < 0:
-            raise ValueError("rmsnorm_quant_fused: bad H for this format")
-        out = (torch.empty_like(x), torch.empty_like(x),
-               torch.empty((T, pw), dtype=torch.uint8, device=dev),
-               torch.empty(nb, dtype=torch.uint8, device=dev))
-    res_out, norm_out, payload, scales = out
-    rc = lib().rmsnorm_quant_fused(fmt, layout, x.data_ptr(), residual.data_ptr(),
-                                   gamma.data_ptr(), float(eps), T, H, _ptr(global_scale),
-                                   res_out.data_ptr(), norm_out.data_ptr(), payload.data_ptr(),
-                                   scales.data_ptr(), _stream(dev))
-    _check(rc, "rmsnorm_quant_fused")
-    return res_out, norm_out, payload, scales
+    return FusedCall(x, residual, gamma, eps, fmt, layout, global_scale, out)()
 
 
 def scale_swizzle(linear: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -403,10 +453,10 @@ def scale_swizzle(linear: torch.Tensor, out: Optional[torch.Tensor] = None) -> t
     if linear.dim() != 2 or not linear.is_contiguous():
         raise ValueError("linear must be a contiguous [rows, sf_cols] uint8 tensor")
     rows, C = linear.shape
+    n = (-(-rows // 128) * 128) * (-(-C // 4) * 4)
     if out is None:
-        n = (-(-rows // 128) * 128) * (-(-C // 4) * 4)
         out = torch.empty(n, dtype=torch.uint8, device=linear.device)
-    _need_gpu(out, "out", torch.uint8)
+    _check_out(out, "out", torch.uint8, n)
     rc = lib().scale_swizzle(linear.data_ptr(), rows, C, out.data_ptr(), _stream(linear.device))
     _check(rc, "scale_swizzle")
     return out

@@ -214,3 +214,26 @@ def test_fused_grid_invariance(orc, fmt):
                 _fused_check(orc, T, 1024, fmt, mxq.SWIZZLED, seed=T)
     finally:
         mxq.set_max_workgroups(0)
+
+
+def test_binding_rejects_small_outputs():
+    """Outputs smaller than the call writes are refused before any launch."""
+    x = torch.zeros(64, 256, dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(1, dtype=torch.float32, device=DEV)
+    small = torch.empty(10, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        mxq.nvfp4_quant_split(x, [64], g, mxq.SWIZZLED, payload=small)
+    with pytest.raises(ValueError):
+        mxq.mxfp8_quant_split(x, [64], mxq.LINEAR, scales=small)
+    with pytest.raises(ValueError):
+        mxq.nvfp4_quant_split_row_scaled(x, [64], mxq.LINEAR,
+                                         row_amax=torch.empty(3, device=DEV))
+    r = torch.zeros_like(x)
+    gm = torch.ones(256, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        mxq.rmsnorm_quant_fused(x, r, gm, out=(torch.empty_like(x), torch.empty_like(x),
+                                               small, small))
+    with pytest.raises(ValueError):
+        mxq.scale_swizzle(torch.zeros(64, 8, dtype=torch.uint8, device=DEV), small)
+    with pytest.raises(ValueError):
+        mxq.mx_quant_grouped(mxq.MXFP8, mxq.LINEAR, [x], payloads=[small])
