@@ -332,6 +332,27 @@ def extra_workloads(torch, mxq, workloads, dev):
         "overhead_per_extra_launch_us": round((ts - tg) / (len(single) - len(grouped)) * 1e6, 2)}
     del layer, grouped, single
 
+    # the pages' flow for comparison: stack 16 experts into one buffer, then
+    # quantize the stack as one tensor (MXFP8, swizzled; Qwen3-235B gate_up)
+    r, c = workloads.QWEN3_235B_A22B["gate_up"]
+    stack = workloads.expert_stack(G, r, c, std=0.015, seed=5000, device=dev)
+    experts = [stack[i].clone() for i in range(G)]  # separate allocations, as in a model
+    flat = torch.empty(G * r, c, dtype=torch.bfloat16, device=dev)
+    in_place = mxq.GroupedCall(0, 1, experts)
+    one_tensor = mxq.GroupedCall(0, 1, [flat])
+
+    def stack_then_quantize(i):
+        torch.stack(experts, out=flat.view(G, r, c))
+        one_tensor(stream)
+    ts = timed(torch, stack_then_quantize, 20)
+    tq = timed(torch, lambda i: one_tensor(stream), 20)
+    tg = timed(torch, lambda i: in_place(stream), 20)
+    nb = G * (r * c * 3 + mxq.scale_bytes(r, c, 0, 1))
+    res["stack_vs_descriptor_qwen3_235b_gate_up_mxfp8"] = {
+        "alg_bytes": nb, "descriptor_table_us": round(tg * 1e6, 1),
+        "stack_then_quantize_us": round(ts * 1e6, 1), "quantize_stacked_only_us": round(tq * 1e6, 1)}
+    del stack, experts, flat, in_place, one_tensor
+
     # NVFP4 with encode scales from the data, same call (amax pass + quantize):
     # one Qwen3-235B-A22B gate_up launch of 16 experts, swizzled
     r, c = workloads.QWEN3_235B_A22B["gate_up"]

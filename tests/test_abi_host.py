@@ -228,3 +228,20 @@ def test_grouped_auto_validation():
     assert _auto([e], cols=40) == ESHAPE                   # 40 % 16
     assert _auto([e] * 17, n_slots=16, slots=[0] * 17) == EINVAL
     assert _auto([_ent(src=0)]) == EINVAL
+
+
+def test_header_compiles_as_c99_and_links(tmp_path):
+    """include/mxq.h is a C header: a C99 client compiled with gcc links the
+    library and sees the documented sizes and statuses."""
+    import subprocess
+    src = os.path.join(ROOT, "tests", "abi_c", "check_abi.c")
+    exe = str(tmp_path / "check_abi")
+    libdir = os.path.dirname(mxq.library_path())
+    subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), src, "-o", exe,
+                    "-L", libdir, "-l:libmxq.so", "-Wl,-rpath," + libdir], check=True)
+    env = dict(os.environ)
+    env["LD_LIBRARY_PATH"] = libdir + ":/opt/rocm/lib:" + env.get("LD_LIBRARY_PATH", "")
+    p = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert p.returncode == 0, p.stdout + p.stderr
+    assert "ok: 0 failed" in p.stdout
