@@ -2,9 +2,10 @@
 // the linear -> swizzled scale conversion.
 //
 // The epilogue needs whole rows (the RMSNorm sum of squares): two or four
-// waves own one row and hold it in registers; a unit is 4 rows.  Swizzled units take
-// rows band*128 + 32*q + gi (gi = 0..31), so a unit writes one 16-byte piece
-// of each tile line (8 consecutive units complete it).  Unit u runs on
+// waves own one row and hold it in registers; a unit is one row (four waves
+// per row) or four rows (two waves per row; swizzled units take rows
+// band*128 + 32*q + gi, gi = 0..31, so a unit writes one 16-byte piece of each
+// tile line and 8 consecutive units complete it).  Unit u runs on
 // workgroup u in plain dispatch order; every byte has one writer.
 #include "mxq_device.h"
 #include "mxq_internal.h"
@@ -62,16 +63,19 @@ __device__ __forceinline__ void flush_interleaved_swz(const uint8_t *stage, uint
 // Fused residual add + RMSNorm + quantize.  The row's bf16 residual sum stays
 // in registers; the sum of squares is each wave's fixed-order partial, the
 // row's WPR partials added in wave order; norm_out and the quantized form come
-// from the same bf16 values.  NCHW: 512-column steps per wave.  With two waves
-// per row the kernel is held to 128 VGPRs, so two workgroups share a CU.
-template <int FMT, int LAYOUT, int NCHW, int WPR>
-__global__ __launch_bounds__(kRowUnit * WPR * kWave)
+// from the same bf16 values.  NCHW: 512-column steps per wave.  A unit is RPU
+// rows: 4 (swizzled rows band*128 + 32*q + gi, whose codes fill one 16-byte
+// piece of each tile line) or 1 (more, smaller workgroups; swizzled codes
+// leave as 4-byte pieces, padding rows as units of their own).  With two
+// waves per row the kernel is held to 128 VGPRs, so two workgroups share a CU.
+template <int FMT, int LAYOUT, int NCHW, int WPR, int RPU>
+__global__ __launch_bounds__(RPU * WPR * kWave)
 __attribute__((amdgpu_waves_per_eu(WPR == 2 ? 4 : 1)))
 void k_fused(const FusedArgs a) {
     using Tr = FmtTraits<FMT>;
-    constexpr int kNT = kRowUnit * WPR * kWave;
+    constexpr int kNT = RPU * WPR * kWave;
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ float red[kRowUnit * WPR];
+    __shared__ float red[RPU * WPR];
     const int H = a.H;
     uint16_t *gamma_s = reinterpret_cast<uint16_t *>(smem);
     uint8_t *stage = smem + ((2 * H + 15) & ~15);
@@ -86,8 +90,11 @@ void k_fused(const FusedArgs a) {
         *reinterpret_cast<u32x4 *>(gamma_s + k) = *reinterpret_cast<const u32x4 *>(a.gamma + k);
     __syncthreads();
     for (int lu = blockIdx.x; lu < a.total_units; lu += gridDim.x) {
-        const int r = LAYOUT == MXQ_SF_SWIZZLED ? (lu >> 5) * 128 + 32 * q + (lu & 31)
-                                                : lu * 4 + q;
+        int r;
+        if constexpr (RPU == 1)
+            r = lu;
+        else
+            r = LAYOUT == MXQ_SF_SWIZZLED ? (lu >> 5) * 128 + 32 * q + (lu & 31) : lu * 4 + q;
         const bool live = r < a.T;
         const int64_t rb = (int64_t)r * H;
         u32x4 xv[NCHW];
@@ -148,18 +155,39 @@ void k_fused(const FusedArgs a) {
                 const uint32_t code = quant8<FMT>(nv, g, quot, pay);  // whole wave
                 if (col < H) {
                     store_payload<FMT>(a.payload + (int64_t)r * payload_ld, col, pay);
-                    if (leader) stage_code<LAYOUT>(stage, q, col / Tr::kBlock, a.sf_cols, code);
+                    if (leader) {
+                        if constexpr (RPU == 1)
+                            stage[col / Tr::kBlock] = (uint8_t)code;
+                        else
+                            stage_code<LAYOUT>(stage, q, col / Tr::kBlock, a.sf_cols, code);
+                    }
                 }
             }
         } else if (LAYOUT == MXQ_SF_SWIZZLED && part == 0) {
-            stage_zero_row<LAYOUT>(stage, q, lane, a.sf_cols, a.sf_stride);
+            if constexpr (RPU == 1)
+                for (int c = lane; c < a.sf_stride; c += kWave) stage[c] = 0;
+            else
+                stage_zero_row<LAYOUT>(stage, q, lane, a.sf_cols, a.sf_stride);
         }
         __syncthreads();
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+        if constexpr (RPU == 1) {
+            if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+                // this row's 4 codes of every tile: one 4-byte piece per tile
+                const int tiles = a.sf_stride >> 2;
+                uint8_t *base = a.scales + (int64_t)(r >> 7) * tiles * 512 + (r & 31) * 16 +
+                                ((r >> 5) & 3) * 4;
+                for (int t = threadIdx.x; t < tiles; t += kNT)
+                    *reinterpret_cast<uint32_t *>(base + (int64_t)t * 512) =
+                        *reinterpret_cast<const uint32_t *>(stage + t * 4);
+            } else if (live) {
+                copy_out_rows<kNT>(a.scales + (int64_t)r * a.sf_cols, stage, a.sf_cols);
+            }
+        } else if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
             flush_interleaved_swz<kNT>(stage, a.scales, lu, a.sf_stride);
-        else
+        } else {
             copy_out_rows<kNT>(a.scales + (int64_t)lu * 4 * a.sf_cols, stage,
-                          min(4, a.T - lu * 4) * a.sf_cols);
+                               min(4, a.T - lu * 4) * a.sf_cols);
+        }
         __syncthreads();
     }
 }
@@ -203,33 +231,33 @@ static int fused_steps(int64_t H, int wpr) {
     return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 7 ? 7 : n <= 8 ? 8 : 16;
 }
 
-template <int FMT, int LAYOUT, int WPR>
+template <int FMT, int LAYOUT, int WPR, int RPU>
 static void fused_nch(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
-    const dim3 bd(kRowUnit * WPR * kWave);
+    const dim3 bd(RPU * WPR * kWave);
     switch (fused_steps(a.H, WPR)) {
-    case 1: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 1, WPR>), gd, bd, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 2, WPR>), gd, bd, lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 4, WPR>), gd, bd, lds, s, a); break;
-    case 7: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 7, WPR>), gd, bd, lds, s, a); break;
-    case 8: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 8, WPR>), gd, bd, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16, WPR>), gd, bd, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 1, WPR, RPU>), gd, bd, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 2, WPR, RPU>), gd, bd, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 4, WPR, RPU>), gd, bd, lds, s, a); break;
+    case 7: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 7, WPR, RPU>), gd, bd, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 8, WPR, RPU>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_fused<FMT, LAYOUT, 16, WPR, RPU>), gd, bd, lds, s, a); break;
     }
 }
 
-// Up to 2048 rows, four waves per row (shorter per-row chains: latency bound);
-// beyond, two waves per row in half the threads (more workgroups per CU:
-// bandwidth bound).  Measured on H = 7168.
+// The shape is the host's choice (a.wpr, a.rpu): four waves per row and
+// one-row units for latency-bound calls (short per-row chains, many
+// workgroups), two waves per row and four-row units for large ones.
 template <int FMT, int LAYOUT>
 static void fused_wpr(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
-    if (a.T <= 2048)
-        fused_nch<FMT, LAYOUT, 4>(a, gd, lds, s);
+    if (a.wpr == 2)
+        fused_nch<FMT, LAYOUT, 2, 4>(a, gd, lds, s);
     else
-        fused_nch<FMT, LAYOUT, 2>(a, gd, lds, s);
+        fused_nch<FMT, LAYOUT, 4, 1>(a, gd, lds, s);
 }
 
 hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s) {
-    // gamma (bf16 [H], 16-byte rounded) then the staged scales of 4 rows
-    const size_t lds = (size_t)((2 * a.H + 15) & ~15) + (size_t)4 * a.sf_stride;
+    // gamma (bf16 [H], 16-byte rounded) then the staged scales of a unit
+    const size_t lds = (size_t)((2 * a.H + 15) & ~15) + (size_t)a.rpu * a.sf_stride;
     const dim3 gd(grid_of(grid));
     if (fmt == MXQ_MXFP8 && layout == MXQ_SF_LINEAR)
         fused_wpr<MXQ_MXFP8, MXQ_SF_LINEAR>(a, gd, lds, s);

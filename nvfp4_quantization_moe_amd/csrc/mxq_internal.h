@@ -83,7 +83,14 @@ struct FusedArgs {
     int32_t sf_cols;
     int32_t sf_stride;
     int32_t total_units;
+    int32_t wpr;          // waves per row: 4 (with rpu 1) or 2 (with rpu 4)
+    int32_t rpu;          // rows per unit
 };
+
+// Fused epilogue shape for T rows: up to this many rows, four waves per row
+// and one-row units (latency bound: short per-row chains, many workgroups);
+// beyond, two waves per row and four-row units (bandwidth bound).
+constexpr int64_t kFusedFourWaveMaxT = 2048;
 
 struct SwizzleArgs {
     const uint8_t *lin;
