@@ -47,6 +47,7 @@ struct GroupArgs {
 };
 
 constexpr int kMaxSplitsPerLaunch = 256;
+constexpr int kSplitScatter = 0;  // SplitArgs::sub of the per-row scatter mode (swizzled)
 
 // Up to 256 consecutive splits of a concatenated activation.  A work unit is
 // 4*sub rows of one expert (swizzled: the rows of one 128-row band that share
@@ -63,9 +64,11 @@ struct SplitArgs {
     int32_t sf_stride;
     int32_t n;            // splits in this launch
     int32_t total_units;
-    int32_t sub;          // rows per tile-line segment: 2 or 8 (linear: 2)
+    int32_t sub;          // swizzled: rows per tile-line segment (2), or 0
+                          // for per-row scatter; linear: 2
     int32_t row_off[kMaxSplitsPerLaunch + 1];   // prefix sums of split rows
     int32_t unit_off[kMaxSplitsPerLaunch + 1];  // prefix sums of split units
+    int32_t band_off[kMaxSplitsPerLaunch + 1];  // prefix sums of 128-row bands
 };
 
 struct FusedArgs {

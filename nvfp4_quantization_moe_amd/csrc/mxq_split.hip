@@ -5,13 +5,16 @@
 // scale, row-scaled NVFP4 (each row under an encode scale derived from its own
 // amax) and MXFP8.
 //
-// Swizzled: a unit owns the SUB-row segment `sub` of line h (0..3) of every
-// scale tile of one 128-row band of one expert, i.e. the rows
-// band*128 + 32*q + 8*h + SUB*sub + i (q < 4, i < SUB), so its staged scales
-// leave as whole 16*SUB-byte segments, padding rows and columns zero.
-// Linear: a unit is 4*SUB consecutive rows.  SUB is 8 (whole 128-byte lines:
-// fewer, fuller units when experts are short) or 2 (more workgroups in
-// flight); the host picks it per call.  Only the unit's live rows are
+// Swizzled, SUB = 2: a unit owns the 2-row segment `sub` of line h (0..3) of
+// every scale tile of one 128-row band of one expert, i.e. the rows
+// band*128 + 32*q + 8*h + 2*sub + i (q < 4, i < 2), so its staged scales leave
+// as whole 32-byte segments, padding rows and columns zero.  Swizzled,
+// SUB = 0 (scatter; for short experts, whose bands are mostly padding): a
+// unit is 8 consecutive rows of one expert and writes each row's 4-byte piece
+// of every tile; one more unit per expert whose last band is partial writes
+// that band's padding rows as zeros (measured faster than 32-row units of
+// whole 128-byte lines: 39-41 against 40-46 us on the routed activation).
+// Linear: a unit is 8 consecutive rows.  The host picks SUB per call.  Only the unit's live rows are
 // loaded: pairs of waves take them in turn, each wave holding half of a row
 // (512-column steps 2k + half) in registers, so short experts keep every wave
 // busy.  A wave loads its next row only after storing the current one:
@@ -29,7 +32,8 @@ template <int FMT, bool ROWSC, int LAYOUT, int NCH2, int SUB>
 __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(NCH2 <= 8 ? 4 : 1)))
 void k_split(const SplitArgs a) {
     using Tr = FmtTraits<FMT>;
-    constexpr int kUnit = 4 * SUB;  // rows per unit
+    constexpr bool kScatter = LAYOUT == MXQ_SF_SWIZZLED && SUB == 0;
+    constexpr int kUnit = kScatter ? 8 : 4 * SUB;  // rows per unit
     extern __shared__ __align__(16) uint8_t stage[];
     __shared__ uint32_t row_max[kUnit];  // one encode scale: row amax folded by LDS atomics
     __shared__ uint32_t half_max[2][8];  // row-scaled: each wave's half-row amax, two buffers
@@ -52,12 +56,35 @@ void k_split(const SplitArgs a) {
         const int lu = u - a.unit_off[s];
         const int m = a.row_off[s + 1] - a.row_off[s];
         const int64_t e0 = a.row_off[s];  // expert's first row
+        const int tiles = a.sf_stride >> 2;
+        if constexpr (kScatter) {
+            // the unit after an expert's row units zeroes the padding rows of
+            // its last band: every 4-byte piece of a row at or past m
+            const int n_row_units = (m + kUnit - 1) / kUnit;
+            if (lu >= n_row_units) {
+                const int b = (m - 1) >> 7;
+                const int lb = m - b * 128;  // live rows in the band, 1..127
+                uint8_t *base = a.scales + (int64_t)(a.band_off[s] + b) * tiles * 512;
+                for (int k = threadIdx.x; k < tiles * 32; k += kSplitThreads) {
+                    const int t = k >> 5, p = k & 31;
+                    const int qf = lb > p ? min(4, (lb - p + 31) / 32) : 0;  // live q's
+                    uint8_t *piece = base + (int64_t)t * 512 + p * 16;
+                    if (qf == 0) {
+                        *reinterpret_cast<u32x4 *>(piece) = u32x4{0, 0, 0, 0};
+                    } else {
+                        for (int q = qf; q < 4; ++q)
+                            *reinterpret_cast<uint32_t *>(piece + q * 4) = 0u;
+                    }
+                }
+                continue;  // uniform over the workgroup
+            }
+        }
         // live rows of the unit, in order; nq[q] of them in line-set row q
         constexpr int kSeg = SUB * 16;  // bytes of each tile the unit fills
         int nq[4] = {0, 0, 0, 0};
         int n_live;
         int band = 0, h = 0, sub = 0;
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED && !kScatter) {
             constexpr int kPerBand = 32 / SUB;
             band = lu / kPerBand;
             h = (lu % kPerBand) / (8 / SUB);
@@ -76,7 +103,7 @@ void k_split(const SplitArgs a) {
         auto locate = [&](int j, int &q, int &i) {
             q = 0;
             i = j;
-            if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            if constexpr (LAYOUT == MXQ_SF_SWIZZLED && !kScatter) {
                 while (i >= nq[q]) { i -= nq[q]; ++q; }
                 return band * 128 + 32 * q + 8 * h + SUB * sub + i;
             } else {
@@ -118,7 +145,9 @@ void k_split(const SplitArgs a) {
                     if (!ROWSC) am = max(am, amax_bits8(cur[k]));
                     if (leader) {
                         const int c = col / Tr::kBlock;
-                        if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
+                        if constexpr (kScatter)
+                            stage[j * a.sf_stride + c] = (uint8_t)code;
+                        else if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
                             stage[(c >> 2) * kSeg + i * 16 + q * 4 + (c & 3)] = (uint8_t)code;
                         else
                             stage[j * a.sf_cols + c] = (uint8_t)code;
@@ -168,8 +197,18 @@ void k_split(const SplitArgs a) {
             const int r = locate(threadIdx.x, q, i);
             a.row_amax[e0 + r] = __uint_as_float(row_max[threadIdx.x] << 16);
         }
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-            const int tiles = a.sf_stride >> 2;
+        if constexpr (kScatter) {
+            // row rl's codes of tile t: the 4-byte piece (rl % 32, rl / 32 % 4)
+            uint8_t *region = a.scales + (int64_t)a.band_off[s] * tiles * 512;
+            for (int k = threadIdx.x; k < n_live * tiles; k += kSplitThreads) {
+                const int j = k / tiles, t = k - (k / tiles) * tiles;
+                const int rl = lu * kUnit + j;
+                *reinterpret_cast<uint32_t *>(region + (int64_t)(rl >> 7) * tiles * 512 +
+                                              (int64_t)t * 512 + (rl & 31) * 16 +
+                                              ((rl >> 5) & 3) * 4) =
+                    *reinterpret_cast<const uint32_t *>(stage + j * a.sf_stride + t * 4);
+            }
+        } else if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
             const int64_t first_band = a.unit_off[s] / (32 / SUB);
             uint8_t *base = a.scales + (first_band + band) * tiles * 512 + h * 128 + sub * kSeg;
             for (int k = threadIdx.x; k < tiles * SUB; k += kSplitThreads) {
@@ -217,12 +256,12 @@ static void split_layout(int layout, const SplitArgs &a, dim3 gd, size_t lds, hi
     else if (a.sub == 2)
         split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED, 2>(a, gd, lds, s);
     else
-        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED, 8>(a, gd, lds, s);
+        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED, 0>(a, gd, lds, s);
 }
 
 hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,
                         hipStream_t s) {
-    const size_t lds = (size_t)4 * a.sub * a.sf_stride;
+    const size_t lds = (size_t)(a.sub == 0 ? 8 : 4 * a.sub) * a.sf_stride;
     const dim3 gd((unsigned)(grid < 1 ? 1 : grid));
     if (fmt == MXQ_MXFP8)
         split_layout<MXQ_MXFP8, false>(layout, a, gd, lds, s);
