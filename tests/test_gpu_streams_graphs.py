@@ -1,0 +1,138 @@
+"""The library keeps no per-call state: calls replay from HIP graphs, run on
+several streams at once, and come from several host threads, with the bytes
+of eager single-stream calls.
+
+Graph replays run several times with eager work and synchronizations in
+between, and every replay is checked (the graphs hold kernel nodes only).
+"""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_quantization_moe_amd as mxq
+from nvfp4_quantization_moe_amd import workloads
+from helpers import bf16_bits
+from gpu_common import CANARY, g_of, say, u8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def raw(t):
+    """Bytes of a tensor of any dtype (bf16 included), as numpy uint8."""
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
+
+
+def _capture(fn):
+    """Warm fn up on a side stream, then capture it into a graph there."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def _replay_and_check(graph, outs, want):
+    for rep in range(3):
+        for t in outs:
+            t.fill_(CANARY) if t.dtype == torch.uint8 else t.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, w in zip(outs, want):
+            assert np.array_equal(raw(t), w), rep
+
+
+@pytest.mark.parametrize("mode", ["nvfp4", "nvfp4_row_scaled", "mxfp8"])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_split_graph_replay(mode, layout):
+    x_cpu, split = workloads.routed_activation(T=2048, H=1024, seed=7)
+    x = x_cpu.to(DEV)
+    g = g_of(x)
+    call = mxq.SplitCall(mode, x, split, layout, g if mode == "nvfp4" else None)
+    say("split graph", mode, layout)
+    eager = [raw(t).copy() for t in call()]
+    graph = _capture(call)
+    _replay_and_check(graph, list(call()), eager)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("T", [3, 3000])
+def test_fused_graph_replay(fmt, T):
+    x, r, gm = (t.to(DEV) for t in workloads.epilogue_inputs(T, 2048, seed=T))
+    gs = torch.tensor([50.0], dtype=torch.float32, device=DEV)
+    call = mxq.FusedCall(x, r, gm, 1e-6, fmt, mxq.SWIZZLED, gs)
+    say("fused graph", fmt, T)
+    eager = [raw(t).copy() for t in call()]
+    graph = _capture(call)
+    _replay_and_check(graph, list(call.out), eager)
+
+
+def test_calls_on_two_streams_at_once():
+    xs = [x.to(DEV) for x in workloads.small_grouped_experts(n_experts=16, rows=512, cols=2048,
+                                                             seed=3)]
+    gs = torch.cat([g_of(x) for x in xs])
+    say("two streams")
+    want = [u8(t).copy() for t in
+            sum(mxq.mx_quant_grouped(mxq.NVFP4, mxq.SWIZZLED, xs, global_scales=gs), [])]
+    calls = [mxq.GroupedCall(mxq.NVFP4, mxq.SWIZZLED, xs[k::2], global_scales=gs[k::2].contiguous())
+             for k in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    torch.cuda.synchronize()
+    for _ in range(5):
+        for c, s in zip(calls, streams):
+            with torch.cuda.stream(s):
+                c()
+    torch.cuda.synchronize()
+    pays = [None] * 16
+    scs = [None] * 16
+    for k, c in enumerate(calls):
+        for j, (p, sc) in enumerate(zip(c.payloads, c.scales)):
+            pays[k + 2 * j], scs[k + 2 * j] = p, sc
+    got = [u8(t) for t in pays + scs]
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+
+
+def test_calls_from_several_host_threads(orc):
+    """Each host thread drives its own stream; ctypes releases the GIL during
+    the library call, so the calls overlap in the library."""
+    n = 4
+    inputs = [workloads.epilogue_inputs(64, 1024, seed=100 + k, device=DEV) for k in range(n)]
+    gs = torch.tensor([80.0], dtype=torch.float32, device=DEV)
+    calls = [mxq.FusedCall(*inputs[k], 1e-6, k % 2, mxq.SWIZZLED, gs) for k in range(n)]
+    streams = [torch.cuda.Stream() for _ in range(n)]
+    errors = []
+    torch.cuda.synchronize()
+    say("host threads")
+
+    def work(k):
+        try:
+            with torch.cuda.stream(streams[k]):
+                for _ in range(20):
+                    calls[k]()
+            streams[k].synchronize()
+        except Exception as e:  # reported below
+            errors.append(e)
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(n)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for k in range(n):
+        x, r, gm = (t.cpu() for t in inputs[k])
+        oro, ono = orc.add_rmsnorm(bf16_bits(x), bf16_bits(r), bf16_bits(gm), 1e-6)
+        ro, no_gpu, p, s = calls[k].out
+        assert np.array_equal(bf16_bits(ro), oro)
+        d = np.abs(bf16_bits(no_gpu).astype(np.int32) - ono.astype(np.int32))
+        assert d.max() <= 1  # N(0,1) inputs: no sign changes near zero matter here
+        qp, qs = orc.quantize(k % 2, mxq.SWIZZLED, bf16_bits(no_gpu), g=80.0)
+        assert np.array_equal(u8(p), qp.ravel()) and np.array_equal(u8(s), qs)
