@@ -14,14 +14,18 @@
 // in LDS.  With the swizzled layout the unit's rows are band*128 + 32*wave +
 // R*h + i (R = kRowsPerWave, i < R) of one 128-row band, which fill one
 // contiguous R*16-byte segment of each 512-byte tile the chunk touches, so
-// scales leave in whole segments, padding included.
+// scales leave in whole segments, padding included.  Measured alternatives
+// that lost: 2 rows per wave (4 or 8 waves), scale codes stored from
+// registers as 4-byte pieces instead of LDS-staged 16-byte segments, a
+// persistent grid with software-pipelined loads.
 //
 // Unit u runs on workgroup u, in plain dispatch order; the hardware spreads
 // consecutive workgroups over the 8 XCDs, so the units in flight cover one
 // contiguous stretch of every tensor (measured faster than giving each XCD a
-// contiguous range).  No global atomics, no scratch, no inter-workgroup
-// ordering: every byte has one writer, and the bytes do not depend on the
-// grid size.
+// contiguous range).  The quantize kernel uses no global atomics, no scratch
+// and no inter-workgroup ordering: every byte has one writer, and the bytes
+// do not depend on the grid size.  (k_amax, for encode scales from the data,
+// folds each workgroup's maximum into its slot with one atomic max.)
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
