@@ -13,10 +13,10 @@
 namespace mxq {
 
 // ---------------------------------------------------------------------------
-// A unit is 4 rows; WPR waves share each row, wave `part` holding the
-// 512-column steps WPR*k + part of it in registers.  gamma is staged in LDS
-// once per workgroup.  Staged scales: swizzled [tile][row][4] (16 bytes per
-// tile), linear [row][C].
+// WPR waves share each row, wave `part` holding the 512-column steps
+// WPR*k + part of it in registers.  gamma is staged in LDS once per
+// workgroup.  Staged scales of a four-row unit: swizzled [tile][row][4]
+// (16 bytes per tile), linear [row][C]; of a one-row unit: the row's codes.
 // ---------------------------------------------------------------------------
 
 template <int LAYOUT>

@@ -14,13 +14,14 @@
 // of every tile; one more unit per expert whose last band is partial writes
 // that band's padding rows as zeros (measured faster than 32-row units of
 // whole 128-byte lines: 39-41 against 40-46 us on the routed activation).
-// Linear: a unit is 8 consecutive rows.  The host picks SUB per call.  Only the unit's live rows are
-// loaded: pairs of waves take them in turn, each wave holding half of a row
-// (512-column steps 2k + half) in registers, so short experts keep every wave
-// busy.  A wave loads its next row only after storing the current one:
-// loading it earlier doubles the row registers and measured slower than
-// leaving the overlap to the other resident waves.  Units run in plain
-// dispatch order; every byte has one writer, and no global atomics are used.
+// Linear: a unit is 8 consecutive rows.  The host picks SUB per call.  Only
+// the unit's live rows are loaded: pairs of waves take them in turn, each
+// wave holding half of a row (512-column steps 2k + half) in registers, so
+// short experts keep every wave busy.  A wave loads its next row only after
+// storing the current one: loading it earlier doubles the row registers and
+// measured slower than leaving the overlap to the other resident waves.
+// Units run in plain dispatch order; every byte has one writer, and no
+// global atomics are used.
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
