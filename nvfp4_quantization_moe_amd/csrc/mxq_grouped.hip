@@ -143,16 +143,28 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
 
 // ---------------------------------------------------------------------------
 // Per-slot amax for encode scales from the data.  A workgroup folds a run of
-// kAmaxUnits consecutive k_grouped units into one value per slot and makes
-// one atomic max per slot it touched: atomics on one address from every
-// workgroup serialize (one per unit measured 4x slower than the whole read),
-// so the run length sets their number.  The amax is kept as fp32 bits (a
-// bf16 magnitude shifted up), whose unsigned order is the value order.  The
-// quantize pass reads the input again from HBM: walking the units in either
-// order, in calls of 1 to 16 experts, showed no reuse from the last-level
-// cache.
+// kAmaxUnits k_grouped units of one entry into one value and makes one atomic
+// max on its slot: atomics on one address from every workgroup serialize (one
+// per unit measured 4x slower than the whole read), so the run length sets
+// their number.  A run takes every W-th unit of its entry (W = the entry's
+// run count), so the runs in flight read a compact window of each entry:
+// runs of consecutive units, which spread the workgroups in flight over the
+// whole tensor, read 7% slower.  The amax is kept as fp32 bits (a bf16
+// magnitude shifted up), whose unsigned order is the value order.  The
+// quantize pass reads the input again from HBM: no unit order, call size (1
+// to 16 experts) or load kind showed reuse from the last-level cache.
 // ---------------------------------------------------------------------------
-constexpr int kAmaxUnits = 16;
+constexpr int kAmaxUnits = 32;
+
+// Runs of an amax launch: ceil(units / kAmaxUnits) per entry.
+__host__ __device__ inline int amax_runs(const GroupArgs &a) {
+    int n_runs = 0;
+    for (int e = 0; e < a.n; ++e) {
+        const int nu = (e + 1 < a.n ? a.e[e + 1].unit_begin : a.total_units) - a.e[e].unit_begin;
+        n_runs += (nu + kAmaxUnits - 1) / kAmaxUnits;
+    }
+    return n_runs;
+}
 
 __global__ __launch_bounds__(64) void k_zero_slots(uint32_t *amax_bits, int n) {
     if ((int)threadIdx.x < n) amax_bits[threadIdx.x] = 0;
@@ -173,25 +185,22 @@ __global__ __launch_bounds__(kThreads) void k_amax(const GroupArgs a) {
         }
         __syncthreads();
     };
-    const int n_runs = (a.total_units + kAmaxUnits - 1) / kAmaxUnits;
+    // runs: each entry's units are split into ceil(n / kAmaxUnits) runs; run lr
+    // of an entry with W runs takes its units lr, lr + W, lr + 2W, ... so that
+    // the runs in flight cover a compact window of every entry
+    const int n_runs = amax_runs(a);
     for (int run = blockIdx.x; run < n_runs; run += gridDim.x) {
-        const int lo = run * kAmaxUnits;  // units [lo, hi)
-        const int hi = min(a.total_units, lo + kAmaxUnits);
-        int ei = 0;
-        while (ei + 1 < a.n && lo >= a.e[ei + 1].unit_begin) ++ei;
-        int slot = a.e[ei].slot;
+        int ei = 0, rb = 0, W = 0, nu = 0;
+        for (;; ++ei) {
+            nu = (ei + 1 < a.n ? a.e[ei + 1].unit_begin : a.total_units) - a.e[ei].unit_begin;
+            W = (nu + kAmaxUnits - 1) / kAmaxUnits;
+            if (run < rb + W) break;
+            rb += W;
+        }
+        const GEntry &E = a.e[ei];
+        const int lr = run - rb;
         uint32_t m = 0;
-        for (int u = lo; u < hi; ++u) {
-            if (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) {  // crossed into a later entry
-                while (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) ++ei;
-                if (a.e[ei].slot != slot) {
-                    flush(m, slot);
-                    m = 0;
-                    slot = a.e[ei].slot;
-                }
-            }
-            const GEntry &E = a.e[ei];
-            const int lu = u - E.unit_begin;
+        for (int lu = lr; lu < nu; lu += W) {
             const int rg = lu / a.n_cc;
             const int col = (lu - rg * a.n_cc) * kChunk + lane * 8;
             u32x4 v[kRowsPerWave];
@@ -200,11 +209,13 @@ __global__ __launch_bounds__(kThreads) void k_amax(const GroupArgs a) {
                 const int r = rg * kUnitRows + kRowsPerWave * q + i;
                 v[i] = u32x4{0, 0, 0, 0};
                 if (r < E.rows && col < a.cols)
-                    v[i] = *reinterpret_cast<const u32x4 *>(E.src + (int64_t)r * E.ld + col);
+                    v[i] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4 *>(E.src + (int64_t)r * E.ld + col));
             }
 #pragma unroll
             for (int i = 0; i < kRowsPerWave; ++i) m = max(m, amax_bits8(v[i]));
         }
+        const int slot = E.slot;
         flush(m, slot);
     }
 }
@@ -236,7 +247,7 @@ hipError_t launch_amax(const GroupArgs &a, int64_t grid, hipStream_t s) {
     hipLaunchKernelGGL(k_zero_slots, dim3(1), dim3(64), 0, s, a.amax_bits, a.n_slots);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.total_units == 0) return err;
-    const int64_t runs = (a.total_units + kAmaxUnits - 1) / kAmaxUnits;
+    const int64_t runs = amax_runs(a);
     hipLaunchKernelGGL(k_amax, dim3(grid_of(grid < runs ? grid : runs)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
