@@ -198,17 +198,6 @@ int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, i
         split_rows = whole;
         n_splits = 1;
     }
-    // Units of 8 rows keep more workgroups in flight.  With swizzled scales
-    // and short experts (under 128 rows on average, so most 128-row bands are
-    // mostly padding) the rows scatter their 4-byte pieces and each partial
-    // band's padding is a unit of its own (sub 0); longer experts take
-    // 8-row segments of the tile lines (sub 2).
-    int sub = 2;
-    if (layout == MXQ_SF_SWIZZLED) {
-        int64_t nonempty = 0;
-        for (int i = 0; i < n_splits; ++i) nonempty += split_rows[i] > 0;
-        if (nonempty > 0 && total_rows < 128 * nonempty) sub = kSplitScatter;
-    }
     int64_t row_base = 0, scale_base = 0;
     for (int first = 0; first < n_splits; first += kMaxSplitsPerLaunch) {
         const int n = n_splits - first < kMaxSplitsPerLaunch ? n_splits - first
@@ -224,26 +213,21 @@ int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, i
         a.sf_cols = (int32_t)C;
         a.sf_stride = (int32_t)Cs;
         a.n = n;
-        a.sub = sub;
-        int64_t rows = 0, units = 0, sbytes = 0, bands = 0;
+        int64_t rows = 0, pads = 0, sbytes = 0, bands = 0;
         for (int j = 0; j < n; ++j) {
             const int64_t m = split_rows[first + j];
             a.row_off[j] = (int32_t)rows;
-            a.unit_off[j] = (int32_t)units;
+            a.unit_off[j] = (int32_t)pads;
             a.band_off[j] = (int32_t)bands;
             rows += m;
             bands += (m + 127) / 128;
-            if (layout == MXQ_SF_LINEAR)  // groups of 4 * sub rows
-                units += (m + 4 * sub - 1) / (4 * sub);
-            else if (sub == kSplitScatter)  // 8-row groups, then the padding unit
-                units += (m + 7) / 8 + (m % 128 != 0 ? 1 : 0);
-            else  // 32 / sub line segments per 128-row band
-                units += (m + 127) / 128 * (32 / sub);
+            pads += layout == MXQ_SF_SWIZZLED && m % 128 != 0 ? 1 : 0;
             sbytes += sf_bytes(m, C, layout);
         }
         a.row_off[n] = (int32_t)rows;
-        a.unit_off[n] = (int32_t)units;
+        a.unit_off[n] = (int32_t)pads;
         a.band_off[n] = (int32_t)bands;
+        const int64_t units = (rows + kSplitUnitRows - 1) / kSplitUnitRows + pads;
         a.total_units = (int32_t)units;
         if (units > 0) {
             hipError_t err =

@@ -47,12 +47,12 @@ struct GroupArgs {
 };
 
 constexpr int kMaxSplitsPerLaunch = 256;
-constexpr int kSplitScatter = 0;  // SplitArgs::sub of the per-row scatter mode (swizzled)
+constexpr int kSplitUnitRows = 8;     // rows per split work unit
 
-// Up to 256 consecutive splits of a concatenated activation.  A work unit is
-// 4*sub rows of one expert (swizzled: the rows of one 128-row band that share
-// a sub-row segment of line h of every scale tile); units never straddle two
-// experts.
+// Up to 256 consecutive splits of a concatenated activation.  Work units
+// [0, ceil(rows / 8)) are 8 consecutive rows of the launch, across split
+// boundaries.  With swizzled scales they are followed by one padding unit per
+// split whose last 128-row band is partial.
 struct SplitArgs {
     const uint16_t *src;  // global row 0 of this launch's first split
     uint8_t *payload;     // same row
@@ -64,10 +64,9 @@ struct SplitArgs {
     int32_t sf_stride;
     int32_t n;            // splits in this launch
     int32_t total_units;
-    int32_t sub;          // swizzled: rows per tile-line segment (2), or 0
-                          // for per-row scatter; linear: 2
+    int32_t pad_;
     int32_t row_off[kMaxSplitsPerLaunch + 1];   // prefix sums of split rows
-    int32_t unit_off[kMaxSplitsPerLaunch + 1];  // prefix sums of split units
+    int32_t unit_off[kMaxSplitsPerLaunch + 1];  // prefix sums of padding units
     int32_t band_off[kMaxSplitsPerLaunch + 1];  // prefix sums of 128-row bands
 };
 

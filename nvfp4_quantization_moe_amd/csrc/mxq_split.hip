@@ -5,22 +5,25 @@
 // scale, row-scaled NVFP4 (each row under an encode scale derived from its own
 // amax) and MXFP8.
 //
-// Swizzled, SUB = 2: a unit owns the 2-row segment `sub` of line h (0..3) of
-// every scale tile of one 128-row band of one expert, i.e. the rows
-// band*128 + 32*q + 8*h + 2*sub + i (q < 4, i < 2), so its staged scales leave
-// as whole 32-byte segments, padding rows and columns zero.  Swizzled,
-// SUB = 0 (scatter; for short experts, whose bands are mostly padding): a
-// unit is 8 consecutive rows of one expert and writes each row's 4-byte piece
-// of every tile; one more unit per expert whose last band is partial writes
-// that band's padding rows as zeros (measured faster than 32-row units of
-// whole 128-byte lines: 39-41 against 40-46 us on the routed activation).
-// Linear: a unit is 8 consecutive rows.  The host picks SUB per call.  Only
-// the unit's live rows are loaded: pairs of waves take them in turn, each
-// wave holding half of a row (512-column steps 2k + half) in registers, so
-// short experts keep every wave busy.  A wave loads its next row only after
-// storing the current one: loading it earlier doubles the row registers and
-// measured slower than leaving the overlap to the other resident waves.
-// Units run in plain dispatch order; every byte has one writer, and no
+// A work unit is 8 consecutive rows of the activation, whatever experts they
+// belong to: consecutive rows are one contiguous stretch of memory, which HBM
+// serves best.  Linear scales of the whole activation are one [rows, C]
+// matrix, so the unit's codes leave as one contiguous run.  With swizzled
+// scales each row's code for tile t is a 4-byte piece at its expert's region,
+// band, line (local row % 32) and slot (local row / 32 % 4); consecutive
+// lanes store consecutive rows, whose pieces share 128-byte lines.  After the
+// row units, one unit per expert whose last band is partial writes that
+// band's padding rows as zeros.  Measured on an [8192, 7168] activation:
+// units of 8 rows of one expert took 39 us (NVFP4, 246 experts of 19-55
+// rows) and units of the 2, 4 or 8-row segments of a band's scale lines
+// (rows 32 apart, whole 32- to 128-byte scale segments) 38-42 us on
+// 150-row experts, against 37.5 and 32 us here.
+//
+// Only the unit's live rows are loaded: pairs of waves take them in turn,
+// each wave holding half of a row (512-column steps 2k + half) in registers.
+// A wave loads its next row only after storing the current one: loading it
+// earlier doubles the row registers and measured slower than leaving the
+// overlap to the other resident waves.  Every byte has one writer, and no
 // global atomics are used.
 #include "mxq_device.h"
 #include "mxq_internal.h"
@@ -29,15 +32,16 @@ namespace mxq {
 
 // Up to 8 half-row steps fit in 128 VGPRs, so two workgroups share a CU;
 // wider rows get the whole register file.
-template <int FMT, bool ROWSC, int LAYOUT, int NCH2, int SUB>
+template <int FMT, bool ROWSC, int LAYOUT, int NCH2>
 __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(NCH2 <= 8 ? 4 : 1)))
 void k_split(const SplitArgs a) {
     using Tr = FmtTraits<FMT>;
-    constexpr bool kScatter = LAYOUT == MXQ_SF_SWIZZLED && SUB == 0;
-    constexpr int kUnit = kScatter ? 8 : 4 * SUB;  // rows per unit
-    extern __shared__ __align__(16) uint8_t stage[];
+    constexpr bool kSwz = LAYOUT == MXQ_SF_SWIZZLED;
+    constexpr int kUnit = kSplitUnitRows;
+    extern __shared__ __align__(16) uint8_t stage[];  // the unit's codes, one row per sf_stride
     __shared__ uint32_t row_max[kUnit];  // one encode scale: row amax folded by LDS atomics
     __shared__ uint32_t half_max[2][8];  // row-scaled: each wave's half-row amax, two buffers
+    __shared__ int64_t row_dst[kUnit];   // swizzled: offset of each row's piece of tile 0
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int pair = w >> 1, half = w & 1;
@@ -45,75 +49,45 @@ void k_split(const SplitArgs a) {
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
     const float g = (FMT == MXQ_NVFP4 && !ROWSC) ? *a.g : 0.0f;
     const float quot = (FMT == MXQ_NVFP4 && !ROWSC) ? nv_wave_quot(g) : 0.0f;
-    const int stage_bytes = kUnit * a.sf_stride;
-    int it = 0;  // row-scaled step counter, uniform over the workgroup
-    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
-        int lo = 0, hi = a.n;  // split s with unit_off[s] <= u < unit_off[s + 1]
+    const int n_rows = a.row_off[a.n];
+    const int n_row_units = (n_rows + kUnit - 1) / kUnit;
+    const int tiles = a.sf_stride >> 2;
+    // last split s in [0, n) with off[s] <= v (empty splits share offsets)
+    auto find = [&](const int32_t *off, int v) {
+        int lo = 0, hi = a.n;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (a.unit_off[mid] <= u) lo = mid; else hi = mid;
+            if (off[mid] <= v) lo = mid; else hi = mid;
         }
-        const int s = lo;
-        const int lu = u - a.unit_off[s];
-        const int m = a.row_off[s + 1] - a.row_off[s];
-        const int64_t e0 = a.row_off[s];  // expert's first row
-        const int tiles = a.sf_stride >> 2;
-        if constexpr (kScatter) {
-            // the unit after an expert's row units zeroes the padding rows of
-            // its last band: every 4-byte piece of a row at or past m
-            const int n_row_units = (m + kUnit - 1) / kUnit;
-            if (lu >= n_row_units) {
-                const int b = (m - 1) >> 7;
-                const int lb = m - b * 128;  // live rows in the band, 1..127
-                uint8_t *base = a.scales + (int64_t)(a.band_off[s] + b) * tiles * 512;
-                for (int k = threadIdx.x; k < tiles * 32; k += kSplitThreads) {
-                    const int t = k >> 5, p = k & 31;
-                    const int qf = lb > p ? min(4, (lb - p + 31) / 32) : 0;  // live q's
-                    uint8_t *piece = base + (int64_t)t * 512 + p * 16;
-                    if (qf == 0) {
-                        *reinterpret_cast<u32x4 *>(piece) = u32x4{0, 0, 0, 0};
-                    } else {
-                        for (int q = qf; q < 4; ++q)
-                            *reinterpret_cast<uint32_t *>(piece + q * 4) = 0u;
-                    }
+        return lo;
+    };
+    int it = 0;  // row-scaled step counter, uniform over the workgroup
+    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
+        if (kSwz && u >= n_row_units) {
+            // padding unit of split s, whose last band is partial: every
+            // 4-byte piece of a band row at or past the split's last row is 0
+            const int s = find(a.unit_off, u - n_row_units);
+            const int m = a.row_off[s + 1] - a.row_off[s];
+            const int b = (m - 1) >> 7;
+            const int lb = m - b * 128;  // live rows in the band, 1..127
+            uint8_t *base = a.scales + (int64_t)(a.band_off[s] + b) * tiles * 512;
+            for (int k = threadIdx.x; k < tiles * 32; k += kSplitThreads) {
+                const int t = k >> 5, p = k & 31;
+                const int qf = lb > p ? min(4, (lb - p + 31) / 32) : 0;  // live q's
+                uint8_t *piece = base + (int64_t)t * 512 + p * 16;
+                if (qf == 0) {
+                    *reinterpret_cast<u32x4 *>(piece) = u32x4{0, 0, 0, 0};
+                } else {
+                    for (int q = qf; q < 4; ++q)
+                        *reinterpret_cast<uint32_t *>(piece + q * 4) = 0u;
                 }
-                continue;  // uniform over the workgroup
             }
+            continue;  // uniform over the workgroup
         }
-        // live rows of the unit, in order; nq[q] of them in line-set row q
-        constexpr int kSeg = SUB * 16;  // bytes of each tile the unit fills
-        int nq[4] = {0, 0, 0, 0};
-        int n_live;
-        int band = 0, h = 0, sub = 0;
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED && !kScatter) {
-            constexpr int kPerBand = 32 / SUB;
-            band = lu / kPerBand;
-            h = (lu % kPerBand) / (8 / SUB);
-            sub = lu % (8 / SUB);
-            const int rb = min(128, m - band * 128);
-            n_live = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                nq[q] = min(SUB, max(0, rb - 32 * q - 8 * h - SUB * sub));
-                n_live += nq[q];
-            }
-        } else {
-            n_live = min(kUnit, m - lu * kUnit);
-        }
-        // j-th live row of the unit -> (line-set row q, slot i, row in expert)
-        auto locate = [&](int j, int &q, int &i) {
-            q = 0;
-            i = j;
-            if constexpr (LAYOUT == MXQ_SF_SWIZZLED && !kScatter) {
-                while (i >= nq[q]) { i -= nq[q]; ++q; }
-                return band * 128 + 32 * q + 8 * h + SUB * sub + i;
-            } else {
-                return lu * kUnit + j;
-            }
-        };
+        const int r0 = u * kUnit;  // the unit's first row in the launch
+        const int n_live = min(kUnit, n_rows - r0);
         auto load_row = [&](int j, u32x4 *v) {
-            int q, i;
-            const uint16_t *src = a.src + (e0 + locate(j, q, i)) * a.cols;
+            const uint16_t *src = a.src + (int64_t)(r0 + j) * a.cols;
 #pragma unroll
             for (int k = 0; k < NCH2; ++k) {
                 const int col = (2 * k + half) * kChunk + lane * 8;
@@ -130,12 +104,10 @@ void k_split(const SplitArgs a) {
             for (int k = 0; k < NCH2; ++k) am = max(am, amax_bits8(cur[k]));
             return wave_max(am);
         };
-        // encode the half row in cur as live row j under (gr, qr); whole wave.
-        // am accumulates the half row's amax bits over the live columns.
+        // encode the half row in cur as row j of the unit under (gr, qr);
+        // whole wave.  am accumulates the half row's amax bits.
         auto encode = [&](int j, float gr, float qr, uint32_t &am) {
-            int q, i;
-            const int r = locate(j, q, i);
-            uint8_t *pay_row = a.payload + (e0 + r) * payload_ld;
+            uint8_t *pay_row = a.payload + (int64_t)(r0 + j) * payload_ld;
 #pragma unroll
             for (int k = 0; k < NCH2; ++k) {
                 const int col = (2 * k + half) * kChunk + lane * 8;
@@ -144,24 +116,31 @@ void k_split(const SplitArgs a) {
                 if (col < a.cols) {
                     store_payload<FMT>(pay_row, col, pay);
                     if (!ROWSC) am = max(am, amax_bits8(cur[k]));
-                    if (leader) {
-                        const int c = col / Tr::kBlock;
-                        if constexpr (kScatter)
-                            stage[j * a.sf_stride + c] = (uint8_t)code;
-                        else if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-                            stage[(c >> 2) * kSeg + i * 16 + q * 4 + (c & 3)] = (uint8_t)code;
-                        else
-                            stage[j * a.sf_cols + c] = (uint8_t)code;
-                    }
+                    if (leader) stage[j * a.sf_stride + col / Tr::kBlock] = (uint8_t)code;
                 }
             }
-            return r;
         };
 
         if (pair < n_live) load_row(pair, cur);
-        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-            for (int k = threadIdx.x * 16; k < stage_bytes; k += kSplitThreads * 16)
-                *reinterpret_cast<u32x4 *>(stage + k) = u32x4{0, 0, 0, 0};
+        if constexpr (kSwz) {
+            // each row's split, its band there, line (local row % 32) and
+            // 4-byte slot (local row / 32 % 4); the splits advance in order
+            int se = find(a.row_off, r0);
+#pragma unroll
+            for (int j = 0; j < kUnit; ++j) {
+                if (j < n_live) {
+                    while (a.row_off[se + 1] <= r0 + j) ++se;
+                    const int rl = r0 + j - a.row_off[se];
+                    if ((int)threadIdx.x == j)
+                        row_dst[j] = (int64_t)(a.band_off[se] + (rl >> 7)) * tiles * 512 +
+                                     (rl & 31) * 16 + ((rl >> 5) & 3) * 4;
+                }
+            }
+            // codes of the padding columns C..round_up(C, 4) stay zero
+            if (a.sf_stride != a.sf_cols) {
+                for (int k = threadIdx.x * 16; k < kUnit * a.sf_stride; k += kSplitThreads * 16)
+                    *reinterpret_cast<u32x4 *>(stage + k) = u32x4{0, 0, 0, 0};
+            }
         }
         if (!ROWSC && threadIdx.x < kUnit) row_max[threadIdx.x] = 0;
         __syncthreads();
@@ -186,39 +165,25 @@ void k_split(const SplitArgs a) {
                     const float af = __uint_as_float(ra << 16);
                     const float gr = nv_encode_scale(af);
                     uint32_t unused = 0;
-                    const int r = encode(j, gr, nv_wave_quot(gr), unused);
-                    if (a.row_amax && half == 0 && lane == 0) a.row_amax[e0 + r] = af;
+                    encode(j, gr, nv_wave_quot(gr), unused);
+                    if (a.row_amax && half == 0 && lane == 0) a.row_amax[r0 + j] = af;
                 }
                 if (j + 4 < n_live) load_row(j + 4, cur);
             }
         }
         __syncthreads();
-        if (!ROWSC && a.row_amax && (int)threadIdx.x < n_live) {
-            int q, i;
-            const int r = locate(threadIdx.x, q, i);
-            a.row_amax[e0 + r] = __uint_as_float(row_max[threadIdx.x] << 16);
-        }
-        if constexpr (kScatter) {
-            // row rl's codes of tile t: the 4-byte piece (rl % 32, rl / 32 % 4)
-            uint8_t *region = a.scales + (int64_t)a.band_off[s] * tiles * 512;
+        if (!ROWSC && a.row_amax && (int)threadIdx.x < n_live)
+            a.row_amax[r0 + threadIdx.x] = __uint_as_float(row_max[threadIdx.x] << 16);
+        if constexpr (kSwz) {
+            // row j's codes of tile t; consecutive lanes take consecutive
+            // rows, whose pieces share 128-byte lines
             for (int k = threadIdx.x; k < n_live * tiles; k += kSplitThreads) {
-                const int j = k / tiles, t = k - (k / tiles) * tiles;
-                const int rl = lu * kUnit + j;
-                *reinterpret_cast<uint32_t *>(region + (int64_t)(rl >> 7) * tiles * 512 +
-                                              (int64_t)t * 512 + (rl & 31) * 16 +
-                                              ((rl >> 5) & 3) * 4) =
+                const int t = k / n_live, j = k - t * n_live;
+                *reinterpret_cast<uint32_t *>(a.scales + row_dst[j] + (int64_t)t * 512) =
                     *reinterpret_cast<const uint32_t *>(stage + j * a.sf_stride + t * 4);
             }
-        } else if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-            const int64_t first_band = a.unit_off[s] / (32 / SUB);
-            uint8_t *base = a.scales + (first_band + band) * tiles * 512 + h * 128 + sub * kSeg;
-            for (int k = threadIdx.x; k < tiles * SUB; k += kSplitThreads) {
-                const int t = k / SUB, part = k % SUB;
-                *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512 + part * 16) =
-                    *reinterpret_cast<const u32x4 *>(stage + t * kSeg + part * 16);
-            }
         } else {
-            uint8_t *dst = a.scales + (e0 + lu * kUnit) * a.sf_cols;
+            uint8_t *dst = a.scales + (int64_t)r0 * a.sf_cols;
             const int nbytes = n_live * a.sf_cols;
             if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
                 for (int k = threadIdx.x; k < (nbytes >> 4); k += kSplitThreads)
@@ -237,32 +202,30 @@ void k_split(const SplitArgs a) {
 // ---------------------------------------------------------------------------
 // Launcher.
 // ---------------------------------------------------------------------------
-template <int FMT, bool ROWSC, int LAYOUT, int SUB>
+template <int FMT, bool ROWSC, int LAYOUT>
 static void split_nch(const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
     const dim3 bd(kSplitThreads);
     switch (half_row_steps(a.cols)) {
-    case 1: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 1, SUB>), gd, bd, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 2, SUB>), gd, bd, lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 4, SUB>), gd, bd, lds, s, a); break;
-    case 7: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 7, SUB>), gd, bd, lds, s, a); break;
-    case 8: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 8, SUB>), gd, bd, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 16, SUB>), gd, bd, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 1>), gd, bd, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 2>), gd, bd, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 4>), gd, bd, lds, s, a); break;
+    case 7: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 7>), gd, bd, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 8>), gd, bd, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 16>), gd, bd, lds, s, a); break;
     }
 }
 
 template <int FMT, bool ROWSC>
 static void split_layout(int layout, const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
     if (layout == MXQ_SF_LINEAR)
-        split_nch<FMT, ROWSC, MXQ_SF_LINEAR, 2>(a, gd, lds, s);
-    else if (a.sub == 2)
-        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED, 2>(a, gd, lds, s);
+        split_nch<FMT, ROWSC, MXQ_SF_LINEAR>(a, gd, lds, s);
     else
-        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED, 0>(a, gd, lds, s);
+        split_nch<FMT, ROWSC, MXQ_SF_SWIZZLED>(a, gd, lds, s);
 }
 
 hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,
                         hipStream_t s) {
-    const size_t lds = (size_t)(a.sub == 0 ? 8 : 4 * a.sub) * a.sf_stride;
+    const size_t lds = (size_t)kSplitUnitRows * a.sf_stride;
     const dim3 gd((unsigned)(grid < 1 ? 1 : grid));
     if (fmt == MXQ_MXFP8)
         split_layout<MXQ_MXFP8, false>(layout, a, gd, lds, s);
