@@ -17,7 +17,10 @@
 // units of 8 rows of one expert took 39 us (NVFP4, 246 experts of 19-55
 // rows) and units of the 2, 4 or 8-row segments of a band's scale lines
 // (rows 32 apart, whole 32- to 128-byte scale segments) 38-42 us on
-// 150-row experts, against 37.5 and 32 us here.
+// 150-row experts, against 37.5 and 32 us here.  Leaving a partial band's
+// codes linear for a second kernel to reorder in place (whole 16-byte chunks,
+// padding included) took 39-41 us: the second launch costs more than the
+// scattered pieces.
 //
 // Only the unit's live rows are loaded: pairs of waves take them in turn,
 // each wave holding half of a row (512-column steps 2k + half) in registers.
