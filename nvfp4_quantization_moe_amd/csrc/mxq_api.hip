@@ -221,7 +221,7 @@ int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, i
             a.band_off[j] = (int32_t)bands;
             rows += m;
             bands += (m + 127) / 128;
-            pads += layout == MXQ_SF_SWIZZLED && m % 128 != 0 ? 1 : 0;
+            pads += layout == MXQ_SF_SWIZZLED && m % 128 != 0 && m % 128 < 32 ? 1 : 0;
             sbytes += sf_bytes(m, C, layout);
         }
         a.row_off[n] = (int32_t)rows;

@@ -52,7 +52,7 @@ constexpr int kSplitUnitRows = 8;     // rows per split work unit
 // Up to 256 consecutive splits of a concatenated activation.  Work units
 // [0, ceil(rows / 8)) are 8 consecutive rows of the launch, across split
 // boundaries.  With swizzled scales they are followed by one padding unit per
-// split whose last 128-row band is partial.
+// split whose last 128-row band has 1..31 live rows.
 struct SplitArgs {
     const uint16_t *src;  // global row 0 of this launch's first split
     uint8_t *payload;     // same row

@@ -9,18 +9,20 @@
 // belong to: consecutive rows are one contiguous stretch of memory, which HBM
 // serves best.  Linear scales of the whole activation are one [rows, C]
 // matrix, so the unit's codes leave as one contiguous run.  With swizzled
-// scales each row's code for tile t is a 4-byte piece at its expert's region,
-// band, line (local row % 32) and slot (local row / 32 % 4); consecutive
-// lanes store consecutive rows, whose pieces share 128-byte lines.  After the
-// row units, one unit per expert whose last band is partial writes that
-// band's padding rows as zeros.  Measured on an [8192, 7168] activation:
-// units of 8 rows of one expert took 39 us (NVFP4, 246 experts of 19-55
-// rows) and units of the 2, 4 or 8-row segments of a band's scale lines
-// (rows 32 apart, whole 32- to 128-byte scale segments) 38-42 us on
-// 150-row experts, against 37.5 and 32 us here.  Leaving a partial band's
-// codes linear for a second kernel to reorder in place (whole 16-byte chunks,
-// padding included) took 39-41 us: the second launch costs more than the
-// scattered pieces.
+// scales each row's code for tile t is a 4-byte slot at its expert's region,
+// band, 16-byte line p = local row % 32 and slot q = local row / 32 % 4.  The
+// last live row of a line also writes the zeros of the padding slots after
+// it, in the same store (16 bytes for a line with one live row), and one
+// unit per expert whose last band has under 32 live rows zeroes the lines
+// with none; consecutive lanes store consecutive rows, whose lines are
+// adjacent.  Measured on an [8192, 7168] activation (NVFP4, 246 experts of
+// 19-55 rows, and 150-row experts): units of 8 rows of one expert, padding
+// written apart in 4-byte slots: 39 us; units of the 2, 4 or 8-row segments
+// of a band's lines (rows 32 apart, whole 32- to 128-byte segments): 38-42 us
+// on 150-row experts; 8 consecutive rows with the padding apart: 37.5 and
+// 32 us; here 35 and 32 us.  Leaving a partial band's codes linear for a
+// second kernel to reorder in place took 39-41 us: the second launch costs
+// more than the scattered slots.
 //
 // Only the unit's live rows are loaded: pairs of waves take them in turn,
 // each wave holding half of a row (512-column steps 2k + half) in registers.
@@ -45,6 +47,7 @@ void k_split(const SplitArgs a) {
     __shared__ uint32_t row_max[kUnit];  // one encode scale: row amax folded by LDS atomics
     __shared__ uint32_t half_max[2][8];  // row-scaled: each wave's half-row amax, two buffers
     __shared__ int64_t row_dst[kUnit];   // swizzled: offset of each row's piece of tile 0
+    __shared__ int32_t row_zero[kUnit];  // swizzled: zero slots the row's store carries
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
     const int pair = w >> 1, half = w & 1;
@@ -67,23 +70,17 @@ void k_split(const SplitArgs a) {
     int it = 0;  // row-scaled step counter, uniform over the workgroup
     for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
         if (kSwz && u >= n_row_units) {
-            // padding unit of split s, whose last band is partial: every
-            // 4-byte piece of a band row at or past the split's last row is 0
+            // padding unit of split s, whose last band has fewer than 32
+            // live rows: the 16-byte chunks with no live row are zeroed
             const int s = find(a.unit_off, u - n_row_units);
             const int m = a.row_off[s + 1] - a.row_off[s];
             const int b = (m - 1) >> 7;
-            const int lb = m - b * 128;  // live rows in the band, 1..127
+            const int lb = m - b * 128;  // live rows in the band, 1..31
             uint8_t *base = a.scales + (int64_t)(a.band_off[s] + b) * tiles * 512;
-            for (int k = threadIdx.x; k < tiles * 32; k += kSplitThreads) {
-                const int t = k >> 5, p = k & 31;
-                const int qf = lb > p ? min(4, (lb - p + 31) / 32) : 0;  // live q's
-                uint8_t *piece = base + (int64_t)t * 512 + p * 16;
-                if (qf == 0) {
-                    *reinterpret_cast<u32x4 *>(piece) = u32x4{0, 0, 0, 0};
-                } else {
-                    for (int q = qf; q < 4; ++q)
-                        *reinterpret_cast<uint32_t *>(piece + q * 4) = 0u;
-                }
+            const int ne = 32 - lb;  // lines p = lb..31 of every tile hold no live row
+            for (int k = threadIdx.x; k < tiles * ne; k += kSplitThreads) {
+                const int t = k / ne, p = lb + k - t * ne;
+                *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512 + p * 16) = u32x4{0, 0, 0, 0};
             }
             continue;  // uniform over the workgroup
         }
@@ -134,9 +131,15 @@ void k_split(const SplitArgs a) {
                 if (j < n_live) {
                     while (a.row_off[se + 1] <= r0 + j) ++se;
                     const int rl = r0 + j - a.row_off[se];
-                    if ((int)threadIdx.x == j)
+                    const int p = rl & 31, q = (rl >> 5) & 3;
+                    // live rows of the band, and the last live slot of line p
+                    const int lb = min(128, a.row_off[se + 1] - a.row_off[se] - (rl & ~127));
+                    const int ql = min(3, (lb - 1 - p) >> 5);
+                    if ((int)threadIdx.x == j) {
                         row_dst[j] = (int64_t)(a.band_off[se] + (rl >> 7)) * tiles * 512 +
-                                     (rl & 31) * 16 + ((rl >> 5) & 3) * 4;
+                                     p * 16 + q * 4;
+                        row_zero[j] = q == ql ? 3 - q : 0;
+                    }
                 }
             }
             // codes of the padding columns C..round_up(C, 4) stay zero
@@ -178,12 +181,22 @@ void k_split(const SplitArgs a) {
         if (!ROWSC && a.row_amax && (int)threadIdx.x < n_live)
             a.row_amax[r0 + threadIdx.x] = __uint_as_float(row_max[threadIdx.x] << 16);
         if constexpr (kSwz) {
-            // row j's codes of tile t; consecutive lanes take consecutive
-            // rows, whose pieces share 128-byte lines
+            // row j's codes of tile t, with the zeros of the padding slots
+            // after it when it is the last live row of its line: one store;
+            // consecutive lanes take consecutive rows, whose lines are adjacent
             for (int k = threadIdx.x; k < n_live * tiles; k += kSplitThreads) {
                 const int t = k / n_live, j = k - t * n_live;
-                *reinterpret_cast<uint32_t *>(a.scales + row_dst[j] + (int64_t)t * 512) =
-                    *reinterpret_cast<const uint32_t *>(stage + j * a.sf_stride + t * 4);
+                const uint32_t c = *reinterpret_cast<const uint32_t *>(stage + j * a.sf_stride + t * 4);
+                uint8_t *dst = a.scales + row_dst[j] + (int64_t)t * 512;
+                switch (row_zero[j]) {
+                case 3: *reinterpret_cast<u32x4 *>(dst) = u32x4{c, 0, 0, 0}; break;
+                case 2:
+                    *reinterpret_cast<uint32_t *>(dst) = c;
+                    *reinterpret_cast<u32x2 *>(dst + 4) = u32x2{0, 0};
+                    break;
+                case 1: *reinterpret_cast<u32x2 *>(dst) = u32x2{c, 0}; break;
+                default: *reinterpret_cast<uint32_t *>(dst) = c; break;
+                }
             }
         } else {
             uint8_t *dst = a.scales + (int64_t)r0 * a.sf_cols;
