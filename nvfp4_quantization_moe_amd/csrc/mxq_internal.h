@@ -15,7 +15,7 @@ constexpr int kRowsPerWave = 4;                // rows per wave in a grouped uni
 constexpr int kUnitRows = 4 * kRowsPerWave;   // rows per grouped work unit
 constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
 constexpr int kRowUnit = 4;    // rows per split/fused work unit
-constexpr int kSplitThreads = 512;  // split workgroup: 8 waves, 2 per row
+constexpr int kSplitThreads = 256;  // split workgroup: 4 waves, 2 per row
 
 // One grouped-launch descriptor.  The whole table travels in the kernel
 // arguments, so a grouped call is one dispatch with no device-side table.
@@ -47,10 +47,10 @@ struct GroupArgs {
 };
 
 constexpr int kMaxSplitsPerLaunch = 256;
-constexpr int kSplitUnitRows = 8;     // rows per split work unit
+constexpr int kSplitUnitRows = 2;     // rows per split work unit
 
 // Up to 256 consecutive splits of a concatenated activation.  Work units
-// [0, ceil(rows / 8)) are 8 consecutive rows of the launch, across split
+// [0, ceil(rows / 2)) are 2 consecutive rows of the launch, across split
 // boundaries.  With swizzled scales they are followed by one padding unit per
 // split whose last 128-row band has 1..31 live rows.
 struct SplitArgs {

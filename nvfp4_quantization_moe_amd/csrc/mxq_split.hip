@@ -5,27 +5,30 @@
 // scale, row-scaled NVFP4 (each row under an encode scale derived from its own
 // amax) and MXFP8.
 //
-// A work unit is 8 consecutive rows of the activation, whatever experts they
-// belong to: consecutive rows are one contiguous stretch of memory, which HBM
-// serves best.  Linear scales of the whole activation are one [rows, C]
-// matrix, so the unit's codes leave as one contiguous run.  With swizzled
-// scales each row's code for tile t is a 4-byte slot at its expert's region,
-// band, 16-byte line p = local row % 32 and slot q = local row / 32 % 4.  The
-// last live row of a line also writes the zeros of the padding slots after
-// it, in the same store (16 bytes for a line with one live row), and one
-// unit per expert whose last band has under 32 live rows zeroes the lines
-// with none; consecutive lanes store consecutive rows, whose lines are
-// adjacent.  Measured on an [8192, 7168] activation (NVFP4, 246 experts of
-// 19-55 rows, and 150-row experts): units of 8 rows of one expert, padding
-// written apart in 4-byte slots: 39 us; units of the 2, 4 or 8-row segments
-// of a band's lines (rows 32 apart, whole 32- to 128-byte segments): 38-42 us
-// on 150-row experts; 8 consecutive rows with the padding apart: 37.5 and
-// 32 us; here 35 and 32 us.  Leaving a partial band's codes linear for a
-// second kernel to reorder in place took 39-41 us: the second launch costs
-// more than the scattered slots.
+// A work unit is 2 consecutive rows of the activation, whatever experts they
+// belong to, taken by a workgroup of 4 waves, two per row.  Consecutive rows
+// are one contiguous stretch of memory, which HBM serves best, and many small
+// workgroups keep the most loads in flight.  Linear scales of the whole
+// activation are one [rows, C] matrix, so the unit's codes leave as one
+// contiguous run.  With swizzled scales each row's code for tile t is a
+// 4-byte slot at its expert's region, band, 16-byte line p = local row % 32
+// and slot q = local row / 32 % 4.  The last live row of a line also writes
+// the zeros of the padding slots after it, in the same store (16 bytes for a
+// line with one live row), and one unit per expert whose last band has under
+// 32 live rows zeroes the lines with none.
 //
-// Only the unit's live rows are loaded: pairs of waves take them in turn,
-// each wave holding half of a row (512-column steps 2k + half) in registers.
+// Measured on an [8192, 7168] activation, NVFP4, swizzled (246 experts of
+// 19-55 rows / experts of 150 rows):
+//   units of 8 rows of one expert, padding apart in 4-byte slots    39 / 39 us
+//   units of a band's 2-, 4- or 8-row line segments (rows 32 apart,
+//     whole 32- to 128-byte scale segments)                          40-45 / 38-42
+//   8 consecutive rows (512 threads), padding apart                   37.5 / 32
+//   same, padding carried by the last live row of each line           35 / 32
+//   same, linear codes of partial bands reordered by a 2nd kernel     39-41 / 39-41
+//   4 consecutive rows (512 or 256 threads)                           33-34.6 / 29.4-31
+//   2 consecutive rows (256 threads; here)                            33.3-34.4 / 29.1
+//   1 row (128 threads)                                               38 / 32
+//
 // A wave loads its next row only after storing the current one: loading it
 // earlier doubles the row registers and measured slower than leaving the
 // overlap to the other resident waves.  Every byte has one writer, and no
@@ -35,17 +38,24 @@
 
 namespace mxq {
 
-// Up to 8 half-row steps fit in 128 VGPRs, so two workgroups share a CU;
-// wider rows get the whole register file.
+// Register budgets without spills: up to 7 half-row steps in 96 VGPRs (5
+// waves per SIMD) with one encode scale, in 128 (4) row-scaled; 8 steps in
+// 128 or, row-scaled, 168 (3); wider rows get the whole register file.
+constexpr int split_waves(int nch2, bool rowsc) {
+    return nch2 <= 7 ? (rowsc ? 4 : 5) : nch2 == 8 ? (rowsc ? 3 : 4) : 1;
+}
+
 template <int FMT, bool ROWSC, int LAYOUT, int NCH2>
-__global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(NCH2 <= 8 ? 4 : 1)))
+__global__ __launch_bounds__(kSplitThreads)
+__attribute__((amdgpu_waves_per_eu(split_waves(NCH2, ROWSC))))
 void k_split(const SplitArgs a) {
     using Tr = FmtTraits<FMT>;
     constexpr bool kSwz = LAYOUT == MXQ_SF_SWIZZLED;
     constexpr int kUnit = kSplitUnitRows;
+    constexpr int kPairs = kSplitThreads / 128;  // rows in flight: two waves per row
     extern __shared__ __align__(16) uint8_t stage[];  // the unit's codes, one row per sf_stride
     __shared__ uint32_t row_max[kUnit];  // one encode scale: row amax folded by LDS atomics
-    __shared__ uint32_t half_max[2][8];  // row-scaled: each wave's half-row amax, two buffers
+    __shared__ uint32_t half_max[2][2 * kPairs];  // row-scaled: each wave's half-row amax, two buffers
     __shared__ int64_t row_dst[kUnit];   // swizzled: offset of each row's piece of tile 0
     __shared__ int32_t row_zero[kUnit];  // swizzled: zero slots the row's store carries
     const int lane = threadIdx.x & (kWave - 1);
@@ -151,17 +161,17 @@ void k_split(const SplitArgs a) {
         if (!ROWSC && threadIdx.x < kUnit) row_max[threadIdx.x] = 0;
         __syncthreads();
         if constexpr (!ROWSC) {
-            for (int j = pair; j < n_live; j += 4) {
+            for (int j = pair; j < n_live; j += kPairs) {
                 uint32_t am = 0;
                 encode(j, g, quot, am);
                 am = wave_max(am);
                 if (lane == 0) atomicMax(&row_max[j], am);
-                if (j + 4 < n_live) load_row(j + 4, cur);
+                if (j + kPairs < n_live) load_row(j + kPairs, cur);
             }
         } else {
             // Every wave takes every step (the barrier needs all of them); a
             // row's two halves meet in half_max before either is encoded.
-            for (int j0 = 0; j0 < n_live; j0 += 4, ++it) {
+            for (int j0 = 0; j0 < n_live; j0 += kPairs, ++it) {
                 const int j = j0 + pair;
                 const uint32_t am = j < n_live ? half_amax() : 0u;
                 if (lane == 0) half_max[it & 1][w] = am;
@@ -174,7 +184,7 @@ void k_split(const SplitArgs a) {
                     encode(j, gr, nv_wave_quot(gr), unused);
                     if (a.row_amax && half == 0 && lane == 0) a.row_amax[r0 + j] = af;
                 }
-                if (j + 4 < n_live) load_row(j + 4, cur);
+                if (j + kPairs < n_live) load_row(j + kPairs, cur);
             }
         }
         __syncthreads();
