@@ -26,7 +26,8 @@
 //   same, padding carried by the last live row of each line           35 / 32
 //   same, linear codes of partial bands reordered by a 2nd kernel     39-41 / 39-41
 //   4 consecutive rows (512 or 256 threads)                           33-34.6 / 29.4-31
-//   2 consecutive rows (256 threads; here)                            33.3-34.4 / 29.1
+//   2 consecutive rows (256 threads)                                  33.3-34.4 / 29.1
+//   same, 4 consecutive units on one XCD (here)                       32.1-32.3 / 29.3
 //   1 row (128 threads)                                               38 / 32
 //
 // A wave loads its next row only after storing the current one: loading it
@@ -37,6 +38,17 @@
 #include "mxq_internal.h"
 
 namespace mxq {
+
+// Workgroup b runs on XCD b % 8, and each XCD has its own L2.  Within every
+// block of 32 workgroups, XCD x takes units 4x..4x+3 of the block: the 4
+// units (8 rows) whose swizzled scale codes share 16-byte lines meet in one
+// L2, which merges their partial-line stores.  The tail past the last whole
+// block keeps the plain order.
+__device__ __forceinline__ int xcd_grouped_unit(int b, int n) {
+    constexpr int kG = 4, kBlock = kG * 8;
+    if (b >= n / kBlock * kBlock) return b;
+    return b / kBlock * kBlock + (b & 7) * kG + (b >> 3) % kG;
+}
 
 // Register budgets without spills: up to 7 half-row steps in 96 VGPRs (5
 // waves per SIMD) with one encode scale, in 128 (4) row-scaled; 8 steps in
@@ -78,7 +90,8 @@ void k_split(const SplitArgs a) {
         return lo;
     };
     int it = 0;  // row-scaled step counter, uniform over the workgroup
-    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
+    for (int u0 = blockIdx.x; u0 < a.total_units; u0 += gridDim.x) {
+        const int u = (int)gridDim.x == a.total_units ? xcd_grouped_unit(u0, a.total_units) : u0;
         if (kSwz && u >= n_row_units) {
             // padding unit of split s, whose last band has fewer than 32
             // live rows: the 16-byte chunks with no live row are zeroed
