@@ -91,8 +91,10 @@ struct FusedArgs {
 
 // Fused epilogue shape for T rows: up to this many rows, four waves per row
 // and one-row units (latency bound: short per-row chains, many workgroups);
-// beyond, two waves per row and four-row units (bandwidth bound).
-constexpr int64_t kFusedFourWaveMaxT = 2048;
+// beyond, two waves per row and four-row units (bandwidth bound).  At
+// H = 7168 the two shapes tie near T = 1536; at T = 2048 four-row units are
+// 1-4 us faster.
+constexpr int64_t kFusedFourWaveMaxT = 1536;
 
 struct SwizzleArgs {
     const uint8_t *lin;
