@@ -228,6 +228,11 @@ def main():
             d["ms"] += ms
             d["n"] += k1 - k0
             d["bytes"] += sum(calls[k][4] for k in range(k0, k1))
+    # spread of the per-step GPU time (events at each step's ends)
+    step_ms = sorted(timer.elapsed_ms(n_ev * s, n_ev * s + len(runs)) for s in range(args.steps))
+
+    def pct(p):
+        return round(step_ms[min(len(step_ms) - 1, int(p * len(step_ms)))], 4)
     timer.close()
     per_kernel = {}
     for key, d in per.items():
@@ -261,6 +266,7 @@ def main():
         "dtype": "fp32",
         "data": "synthetic",
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "step_ms_gpu": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
         "config": {
             "workload": "Qwen3-235B-A22B-shaped MoE layer: 128 experts gate_up bf16 [3072,4096] "
                         "+ 128 down bf16 [4096,1536], N(0,0.015^2) with 1e-4 outliers x50; "
@@ -280,17 +286,21 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def timed(torch, fn, iters, warm=3):
+def timed(torch, fn, iters, warm=3, reps=5):
+    """Seconds per call: the median over `reps` blocks of `iters` calls."""
     for _ in range(warm):
         fn(0)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(iters):
-        fn(i)
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters * 1e-3  # seconds per iteration
+    per = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(iters):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / iters * 1e-3)
+    return sorted(per)[len(per) // 2]
 
 
 def extra_workloads(torch, mxq, workloads, dev):
