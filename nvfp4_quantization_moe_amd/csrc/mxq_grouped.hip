@@ -19,10 +19,11 @@
 // registers as 4-byte pieces instead of LDS-staged 16-byte segments, a
 // persistent grid with software-pipelined loads.
 //
-// Unit u runs on workgroup u, in plain dispatch order; the hardware spreads
-// consecutive workgroups over the 8 XCDs, so the units in flight cover one
-// contiguous stretch of every tensor (measured faster than giving each XCD a
-// contiguous range).  The quantize kernel uses no global atomics, no scratch
+// Unit u runs on workgroup u, in plain dispatch order, except that with
+// linear scales every 8 consecutive units run on one XCD (1-3 % faster; no
+// gain swizzled, whose units write whole scale segments); the units in flight
+// cover one contiguous stretch of every tensor (measured faster than giving
+// each XCD a contiguous range).  The quantize kernel uses no global atomics, no scratch
 // and no inter-workgroup ordering: every byte has one writer, and the bytes
 // do not depend on the grid size.  (k_amax, for encode scales from the data,
 // folds each workgroup's maximum into its slot with one atomic max.)
@@ -61,7 +62,12 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
     if (AUTO && blockIdx.x == 0 && (int)threadIdx.x < a.n_slots)
         a.g_out[threadIdx.x] = nv_encode_scale(__uint_as_float(a.amax_bits[threadIdx.x]));
-    for (int u = blockIdx.x; u < a.total_units; u += gridDim.x) {
+    for (int u0 = blockIdx.x; u0 < a.total_units; u0 += gridDim.x) {
+        // linear: 8 consecutive units (the column chunks of a row group) share
+        // 128-byte scale lines; meeting in one L2 merges their partial lines
+        const int u = LAYOUT == MXQ_SF_LINEAR && (int)gridDim.x == a.total_units
+                          ? xcd_grouped_unit<8>(u0, a.total_units)
+                          : u0;
         int ei = 0;
         while (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) ++ei;
         const GEntry &E = a.e[ei];

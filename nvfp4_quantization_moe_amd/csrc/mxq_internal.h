@@ -17,6 +17,18 @@ constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
 constexpr int kRowUnit = 4;    // rows per split/fused work unit
 constexpr int kSplitThreads = 256;  // split workgroup: 4 waves, 2 per row
 
+// Workgroup b of a launch runs on XCD b % 8, and each XCD has its own L2.
+// Within every block of 8*G workgroups, XCD x takes units G*x .. G*x + G-1 of
+// the block, so G consecutive units, which write neighbouring bytes, meet in
+// one L2 while the units in flight still cover one compact window.  The tail
+// past the last whole block keeps the plain order.
+template <int G>
+__device__ __forceinline__ int xcd_grouped_unit(int b, int n) {
+    constexpr int kBlock = G * 8;
+    if (b >= n / kBlock * kBlock) return b;
+    return b / kBlock * kBlock + (b & 7) * G + (b >> 3) % G;
+}
+
 // One grouped-launch descriptor.  The whole table travels in the kernel
 // arguments, so a grouped call is one dispatch with no device-side table.
 struct GEntry {

@@ -39,17 +39,6 @@
 
 namespace mxq {
 
-// Workgroup b runs on XCD b % 8, and each XCD has its own L2.  Within every
-// block of 32 workgroups, XCD x takes units 4x..4x+3 of the block: the 4
-// units (8 rows) whose swizzled scale codes share 16-byte lines meet in one
-// L2, which merges their partial-line stores.  The tail past the last whole
-// block keeps the plain order.
-__device__ __forceinline__ int xcd_grouped_unit(int b, int n) {
-    constexpr int kG = 4, kBlock = kG * 8;
-    if (b >= n / kBlock * kBlock) return b;
-    return b / kBlock * kBlock + (b & 7) * kG + (b >> 3) % kG;
-}
-
 // Register budgets without spills: up to 7 half-row steps in 96 VGPRs (5
 // waves per SIMD) with one encode scale, in 128 (4) row-scaled; 8 steps in
 // 128 or, row-scaled, 168 (3); wider rows get the whole register file.
@@ -91,7 +80,9 @@ void k_split(const SplitArgs a) {
     };
     int it = 0;  // row-scaled step counter, uniform over the workgroup
     for (int u0 = blockIdx.x; u0 < a.total_units; u0 += gridDim.x) {
-        const int u = (int)gridDim.x == a.total_units ? xcd_grouped_unit(u0, a.total_units) : u0;
+        // the 4 units (8 rows) whose swizzled codes share 16-byte lines meet in
+        // one L2, which merges their partial-line stores
+        const int u = (int)gridDim.x == a.total_units ? xcd_grouped_unit<4>(u0, a.total_units) : u0;
         if (kSwz && u >= n_row_units) {
             // padding unit of split s, whose last band has fewer than 32
             // live rows: the 16-byte chunks with no live row are zeroed
