@@ -300,8 +300,7 @@ int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual
     a.sf_stride = (int32_t)(layout == MXQ_SF_SWIZZLED ? round_up(C, 4) : C);
     a.wpr = T <= kFusedFourWaveMaxT ? 4 : 2;
     a.rpu = a.wpr == 4 ? 1 : 4;
-    const int64_t units = a.rpu == 1 ? (layout == MXQ_SF_SWIZZLED ? round_up(T, 128) : T)
-                                     : row_groups(T, layout, kRowUnit);
+    const int64_t units = row_groups(T, layout, a.rpu);
     a.total_units = (int32_t)units;
     hipError_t err = launch_fused(fmt, layout, a, grid_for(units), (hipStream_t)stream);
     return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;

@@ -2,11 +2,9 @@
 // the linear -> swizzled scale conversion.
 //
 // The epilogue needs whole rows (the RMSNorm sum of squares): two or four
-// waves own one row and hold it in registers; a unit is one row (four waves
-// per row) or four rows (two waves per row; swizzled units take rows
-// band*128 + 32*q + gi, gi = 0..31, so a unit writes one 16-byte piece of each
-// tile line and 8 consecutive units complete it).  Unit u runs on
-// workgroup u in plain dispatch order; every byte has one writer.
+// waves own one row and hold it in registers.  A unit is RPU consecutive
+// rows; swizzled units cover the padding rows up to the next multiple of 128
+// too.  Every byte has one writer.
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
@@ -15,25 +13,8 @@ namespace mxq {
 // ---------------------------------------------------------------------------
 // WPR waves share each row, wave `part` holding the 512-column steps
 // WPR*k + part of it in registers.  gamma is staged in LDS once per
-// workgroup.  Staged scales of a four-row unit: swizzled [tile][row][4]
-// (16 bytes per tile), linear [row][C]; of a one-row unit: the row's codes.
+// workgroup, then each unit's codes, one row per sf_stride bytes.
 // ---------------------------------------------------------------------------
-
-template <int LAYOUT>
-__device__ __forceinline__ void stage_code(uint8_t *stage, int q, int c, int sf_cols,
-                                           uint32_t code) {
-    if constexpr (LAYOUT == MXQ_SF_SWIZZLED)
-        stage[(c >> 2) * 16 + q * 4 + (c & 3)] = (uint8_t)code;
-    else
-        stage[q * sf_cols + c] = (uint8_t)code;
-}
-
-// Zero the staged codes of a row with no data (swizzled padding rows).
-template <int LAYOUT>
-__device__ __forceinline__ void stage_zero_row(uint8_t *stage, int q, int lane, int sf_cols,
-                                               int sf_stride) {
-    for (int c = lane; c < sf_stride; c += kWave) stage_code<LAYOUT>(stage, q, c, sf_cols, 0);
-}
 
 // Copy n staged bytes to global memory with the whole workgroup (NT threads).
 template <int NT>
@@ -48,26 +29,14 @@ __device__ __forceinline__ void copy_out_rows(uint8_t *dst, const uint8_t *src, 
     }
 }
 
-// Swizzled units take rows band*128 + 32*q + gi (gi = lu mod 32): one
-// 16-byte piece per tile line.
-template <int NT>
-__device__ __forceinline__ void flush_interleaved_swz(const uint8_t *stage, uint8_t *region,
-                                                      int lu, int sf_stride) {
-    const int tiles = sf_stride >> 2;
-    uint8_t *base = region + (int64_t)(lu >> 5) * tiles * 512 + (lu & 31) * 16;
-    for (int t = threadIdx.x; t < tiles; t += NT)
-        *reinterpret_cast<u32x4 *>(base + (int64_t)t * 512) =
-            *reinterpret_cast<const u32x4 *>(stage + t * 16);
-}
-
 // Fused residual add + RMSNorm + quantize.  The row's bf16 residual sum stays
 // in registers; the sum of squares is each wave's fixed-order partial, the
 // row's WPR partials added in wave order; norm_out and the quantized form come
 // from the same bf16 values.  NCHW: 512-column steps per wave.  A unit is RPU
-// rows: 4 (swizzled rows band*128 + 32*q + gi, whose codes fill one 16-byte
-// piece of each tile line) or 1 (more, smaller workgroups; swizzled codes
-// leave as 4-byte pieces, padding rows as units of their own).  With two
-// waves per row the kernel is held to 128 VGPRs, so two workgroups share a CU.
+// consecutive rows; swizzled codes leave as each row's 4-byte slot of every
+// tile, consecutive lanes taking consecutive rows (whose slots share 16-byte
+// lines), and the units that share lines run on one XCD.  With two waves per
+// row the kernel is held to 128 VGPRs.
 template <int FMT, int LAYOUT, int NCHW, int WPR, int RPU>
 __global__ __launch_bounds__(RPU * WPR * kWave)
 __attribute__((amdgpu_waves_per_eu(WPR == 2 ? 4 : 1)))
@@ -81,7 +50,8 @@ void k_fused(const FusedArgs a) {
     uint8_t *stage = smem + ((2 * H + 15) & ~15);
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
-    const int q = w / WPR, part = w % WPR;
+    const int q = RPU == 1 ? 0 : w / WPR;  // the unit's row of this wave (0: scalar addresses)
+    const int part = w % WPR;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
     const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
     const float quot = FMT == MXQ_NVFP4 ? nv_wave_quot(g) : 0.0f;
@@ -89,12 +59,12 @@ void k_fused(const FusedArgs a) {
     for (int k = threadIdx.x * 8; k < H; k += kNT * 8)  // H is a multiple of 16
         *reinterpret_cast<u32x4 *>(gamma_s + k) = *reinterpret_cast<const u32x4 *>(a.gamma + k);
     __syncthreads();
-    for (int lu = blockIdx.x; lu < a.total_units; lu += gridDim.x) {
-        int r;
-        if constexpr (RPU == 1)
-            r = lu;
-        else
-            r = LAYOUT == MXQ_SF_SWIZZLED ? (lu >> 5) * 128 + 32 * q + (lu & 31) : lu * 4 + q;
+    for (int lu0 = blockIdx.x; lu0 < a.total_units; lu0 += gridDim.x) {
+        // the 8 rows whose swizzled codes share 16-byte lines on one XCD
+        const int lu = LAYOUT == MXQ_SF_SWIZZLED && (int)gridDim.x == a.total_units
+                           ? xcd_grouped_unit<8 / RPU>(lu0, a.total_units)
+                           : lu0;
+        const int r = lu * RPU + q;
         const bool live = r < a.T;
         const int64_t rb = (int64_t)r * H;
         u32x4 xv[NCHW];
@@ -155,38 +125,28 @@ void k_fused(const FusedArgs a) {
                 const uint32_t code = quant8<FMT>(nv, g, quot, pay);  // whole wave
                 if (col < H) {
                     store_payload<FMT>(a.payload + (int64_t)r * payload_ld, col, pay);
-                    if (leader) {
-                        if constexpr (RPU == 1)
-                            stage[col / Tr::kBlock] = (uint8_t)code;
-                        else
-                            stage_code<LAYOUT>(stage, q, col / Tr::kBlock, a.sf_cols, code);
-                    }
+                    if (leader) stage[q * a.sf_stride + col / Tr::kBlock] = (uint8_t)code;
                 }
             }
         } else if (LAYOUT == MXQ_SF_SWIZZLED && part == 0) {
-            if constexpr (RPU == 1)
-                for (int c = lane; c < a.sf_stride; c += kWave) stage[c] = 0;
-            else
-                stage_zero_row<LAYOUT>(stage, q, lane, a.sf_cols, a.sf_stride);
+            for (int c = lane; c < a.sf_stride; c += kWave) stage[q * a.sf_stride + c] = 0;
         }
         __syncthreads();
-        if constexpr (RPU == 1) {
-            if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-                // this row's 4 codes of every tile: one 4-byte piece per tile
-                const int tiles = a.sf_stride >> 2;
-                uint8_t *base = a.scales + (int64_t)(r >> 7) * tiles * 512 + (r & 31) * 16 +
-                                ((r >> 5) & 3) * 4;
-                for (int t = threadIdx.x; t < tiles; t += kNT)
-                    *reinterpret_cast<uint32_t *>(base + (int64_t)t * 512) =
-                        *reinterpret_cast<const uint32_t *>(stage + t * 4);
-            } else if (live) {
-                copy_out_rows<kNT>(a.scales + (int64_t)r * a.sf_cols, stage, a.sf_cols);
+        const int r0 = lu * RPU;
+        if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
+            // row r0 + j's 4 codes of tile t: one 4-byte slot per tile
+            const int tiles = a.sf_stride >> 2;
+            for (int k = threadIdx.x; k < tiles * RPU; k += kNT) {
+                const int t = k / RPU, j = k % RPU, rr = r0 + j;
+                uint8_t *dst = a.scales + ((int64_t)(rr >> 7) * tiles + t) * 512 + (rr & 31) * 16 +
+                               ((rr >> 5) & 3) * 4;
+                *reinterpret_cast<uint32_t *>(dst) =
+                    *reinterpret_cast<const uint32_t *>(stage + j * a.sf_stride + t * 4);
             }
-        } else if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
-            flush_interleaved_swz<kNT>(stage, a.scales, lu, a.sf_stride);
-        } else {
-            copy_out_rows<kNT>(a.scales + (int64_t)lu * 4 * a.sf_cols, stage,
-                               min(4, a.T - lu * 4) * a.sf_cols);
+        } else if (r0 < a.T) {
+            // linear: sf_stride == sf_cols, so the live rows' codes are contiguous
+            copy_out_rows<kNT>(a.scales + (int64_t)r0 * a.sf_cols, stage,
+                               min(RPU, a.T - r0) * a.sf_cols);
         }
         __syncthreads();
     }
@@ -246,7 +206,9 @@ static void fused_nch(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
 
 // The shape is the host's choice (a.wpr, a.rpu): four waves per row and
 // one-row units for latency-bound calls (short per-row chains, many
-// workgroups), two waves per row and four-row units for large ones.
+// workgroups), two waves per row and four-row units for large ones.  Units
+// of rows 32 apart (whole 16-byte swizzled pieces per unit) measured 3-6 %
+// slower at T = 4096 than these consecutive rows.
 template <int FMT, int LAYOUT>
 static void fused_wpr(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
     if (a.wpr == 2)
