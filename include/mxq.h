@@ -208,7 +208,8 @@ int mxfp8_quant_split(const void *src, int64_t total_rows, int64_t cols,
  * H is a multiple of 32 (MXFP8) or 16 (NVFP4) and at most 16384; with the
  * swizzled layout H must also give a multiple of 4 scale columns (H % 128 == 0
  * for MXFP8, H % 64 == 0 for NVFP4), else MXQ_ESHAPE.  eps must be finite and
- * > 0.  T == 0 is MXQ_OK with no launch.  All pointers 16-byte aligned.
+ * > 0; 0 <= T <= 2^31 - 128, else MXQ_EINVAL.  T == 0 is MXQ_OK with no
+ * launch.  All pointers 16-byte aligned.
  */
 int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual,
                         const void *gamma, float eps, int64_t T, int64_t H,

@@ -270,7 +270,9 @@ int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual
                         const float *global_scale, void *residual_out, void *norm_out,
                         void *payload, void *scales, void *stream) {
     if (!valid_fmt(fmt) || !valid_layout(layout)) return MXQ_EINVAL;
-    if (!(eps > 0.0f) || !(eps < 3.4e38f) || T < 0 || T >= (int64_t)1 << 31) return MXQ_EINVAL;
+    // rows padded to 128 must still index as int32
+    if (!(eps > 0.0f) || !(eps < 3.4e38f) || T < 0 || T > ((int64_t)1 << 31) - 128)
+        return MXQ_EINVAL;
     if (H <= 0 || H % block_of(fmt) != 0 || H > kMaxFusedH) return MXQ_ESHAPE;
     const int64_t C = H / block_of(fmt);
     // The swizzled tile needs four scale columns; a hidden size that would pad

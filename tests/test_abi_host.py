@@ -177,6 +177,7 @@ def test_fused_validation():
     assert _fused(eps=float("nan")) == EINVAL
     assert _fused(eps=float("inf")) == EINVAL
     assert _fused(T=-1) == EINVAL
+    assert _fused(T=(1 << 31) - 127) == EINVAL      # padded rows must index as int32
     assert _fused(fmt=3) == EINVAL
     assert _fused(H=96) == ESHAPE                   # MXFP8 swizzled: 3 scale cols pad
     assert _fused(H=48) == ESHAPE                   # 48 % 32
