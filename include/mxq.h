@@ -84,7 +84,7 @@ typedef struct {
                                  layout) bytes; 16-byte aligned if swizzled     */
     const float *global_scale;/* device fp32 scalar: NVFP4 encode scale g in
                                  [2^-100, 2^100]; ignored for MXFP8             */
-    int64_t rows;             /* >= 0 and < 2^31; 0 writes nothing             */
+    int64_t rows;             /* 0 .. 2^31 - 128; 0 writes nothing             */
     int64_t src_ld;           /* row stride in elements: >= cols, multiple of 8 */
 } mxq_entry;
 

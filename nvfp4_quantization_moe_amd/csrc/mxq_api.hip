@@ -93,7 +93,8 @@ int pack_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries, in
     int64_t units = 0;
     for (int i = 0; i < n_entries; ++i) {
         const mxq_entry &e = entries[i];
-        if (e.rows < 0 || e.rows >= (int64_t)1 << 31) return MXQ_EINVAL;
+        // rows padded to 128 must still index as int32
+        if (e.rows < 0 || e.rows > ((int64_t)1 << 31) - 128) return MXQ_EINVAL;
         if (e.rows > 0) {
             if (!e.src || !e.payload || !e.scales) return MXQ_EINVAL;
             if (need_g && !e.global_scale) return MXQ_EINVAL;

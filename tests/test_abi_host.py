@@ -93,6 +93,7 @@ def test_grouped_validation():
     assert _grouped(0, 0, 0, [_ent(cols=0)]) == ESHAPE
     assert _grouped(0, 0, 65536, [_ent(cols=65536)]) == ESHAPE    # too wide
     assert _grouped(0, 0, 64, [_ent(rows=-1)]) == EINVAL
+    assert _grouped(0, 1, 64, [_ent(rows=(1 << 31) - 127)]) == EINVAL  # padded rows overflow
     assert _grouped(0, 0, 64, [_ent(src=0)]) == EINVAL            # null src
     assert _grouped(0, 0, 64, [_ent(pay=0)]) == EINVAL
     assert _grouped(0, 0, 64, [_ent(sc=0)]) == EINVAL
