@@ -14,7 +14,6 @@ constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kRowsPerWave = 4;                // rows per wave in a grouped unit
 constexpr int kUnitRows = 4 * kRowsPerWave;   // rows per grouped work unit
 constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
-constexpr int kRowUnit = 4;    // rows per split/fused work unit
 constexpr int kSplitThreads = 256;  // split workgroup: 4 waves, 2 per row
 
 // Workgroup b of a launch runs on XCD b % 8, and each XCD has its own L2.
@@ -127,8 +126,10 @@ hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a
 hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_swizzle(const SwizzleArgs &a, int64_t grid, hipStream_t s);
 
-// Largest supported row length (keeps one unit's staged scales within 32 KiB
-// of LDS, and a split or fused row within registers).
+// Largest supported row lengths.  Grouped units take 512-column chunks, so
+// any width works; these are the widths tested against the oracle.  The split
+// and fused kernels hold a whole row in registers, 16 steps of 512 columns
+// per wave pair at most.
 constexpr int64_t kMaxColsMx = 32768;
 constexpr int64_t kMaxColsNv = 16384;
 constexpr int64_t kMaxSplitCols = 16384;

@@ -104,6 +104,29 @@ def test_ragged_shapes_and_canaries(orc, fmt, layout):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_widest_rows(orc, fmt, layout):
+    """The widest supported rows (32768 MXFP8, 16384 NVFP4 columns), and one
+    block less, whose last 512-column chunk is ragged."""
+    rng = torch.Generator().manual_seed(77 + 10 * fmt + layout)
+    widest = 32768 if fmt == 0 else 16384
+    block = 32 if fmt == 0 else 16
+    for cols in (widest, widest - block):
+        rows = 131
+        say("widest", fmt, layout, rows, cols)
+        xs_cpu = [(torch.randn(rows - 50 * k, cols, generator=rng) *
+                   torch.exp(torch.randn(rows - 50 * k, 1, generator=rng))).to(torch.bfloat16)
+                  for k in range(2)]
+        xs = [x.to(DEV) for x in xs_cpu]
+        gs = torch.cat([g_of(x) for x in xs]) if fmt == 1 else None
+        pays, scs = run_grouped(fmt, layout, xs, gs)
+        for i, x in enumerate(xs_cpu):
+            p, s = oracle_entry(orc, fmt, layout, x, float(gs[i]) if fmt == 1 else 1.0)
+            assert np.array_equal(pays[i], p.ravel()), (cols, i)
+            assert np.array_equal(scs[i], s), (cols, i)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_strided_source_rows(orc, fmt):
     say("strided src", fmt)
     big = (torch.randn(96, 1024) * 3).to(torch.bfloat16)
