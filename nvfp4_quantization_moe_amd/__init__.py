@@ -16,9 +16,11 @@ from typing import List, Optional, Sequence
 import torch
 
 __all__ = [
-    "MXFP8", "NVFP4", "LINEAR", "SWIZZLED", "MAX_GROUP", "MxqError",
-    "mx_quant_grouped", "nvfp4_quant_split", "rmsnorm_quant_fused", "scale_swizzle",
-    "GroupedCall", "scale_bytes", "split_scale_offset", "set_max_workgroups", "library_path", "lib",
+    "MXFP8", "NVFP4", "LINEAR", "SWIZZLED", "MAX_GROUP", "SPLIT_MODES", "MxqError",
+    "mx_quant_grouped", "nvfp4_quant_grouped_auto", "nvfp4_quant_split",
+    "nvfp4_quant_split_row_scaled", "mxfp8_quant_split", "rmsnorm_quant_fused", "scale_swizzle",
+    "GroupedCall", "GroupedAutoCall", "SplitCall", "FusedCall",
+    "scale_bytes", "split_scale_offset", "set_max_workgroups", "library_path", "lib",
 ]
 
 MXFP8, NVFP4 = 0, 1
@@ -209,6 +211,8 @@ class GroupedAutoCall:
         self.layout = layout
         self.srcs = list(srcs)
         n = len(self.srcs)
+        if n == 0:
+            raise ValueError("nvfp4_quant_grouped_auto needs at least one src")
         dummy_g = torch.ones(1, dtype=torch.float32, device=self.srcs[0].device)
         self.payloads, self.scales = _grouped_outputs(NVFP4, layout, self.srcs, payloads, scales,
                                                       dummy_g.expand(n).contiguous())
@@ -223,10 +227,8 @@ class GroupedAutoCall:
         self.g = torch.empty(n_slots, dtype=torch.float32, device=dev) if g_out is None else g_out
         self.amax = (torch.empty(n_slots, dtype=torch.float32, device=dev)
                      if amax_out is None else amax_out)
-        _need_gpu(self.g, "g_out", torch.float32)
-        _need_gpu(self.amax, "amax_out", torch.float32)
-        if self.g.numel() < n_slots or self.amax.numel() < n_slots:
-            raise ValueError("g_out and amax_out need one value per slot")
+        _check_out(self.g, "g_out", torch.float32, n_slots, dev)
+        _check_out(self.amax, "amax_out", torch.float32, n_slots, dev)
         self.cols = self.srcs[0].shape[1]
         self.device = dev
         self._batches = []
@@ -285,6 +287,8 @@ def _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales):
     for i, (s, p, c) in enumerate(zip(srcs, payloads, scales)):
         _need_gpu(p, f"payloads[{i}]", torch.uint8)
         _need_gpu(c, f"scales[{i}]", torch.uint8)
+        if p.device != dev or c.device != dev:
+            raise ValueError(f"payloads[{i}] and scales[{i}] must be on {dev}")
         if p.numel() < s.shape[0] * pw or not p.is_contiguous():
             raise ValueError(f"payloads[{i}] too small or not contiguous")
         if c.numel() < scale_bytes(s.shape[0], cols, fmt, layout) or not c.is_contiguous():
@@ -292,8 +296,10 @@ def _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales):
     return payloads, scales
 
 
-def _check_out(t, name, dtype, numel):
+def _check_out(t, name, dtype, numel, dev):
     _need_gpu(t, name, dtype)
+    if t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
     if not t.is_contiguous() or t.numel() < numel:
         raise ValueError(f"{name}: needs a contiguous tensor of at least {numel} elements")
 
@@ -330,10 +336,10 @@ class SplitCall:
             scales = torch.empty(total, dtype=torch.uint8, device=dev)
         if row_amax is None and (want_row_amax or mode == "nvfp4_row_scaled"):
             row_amax = torch.empty(T, dtype=torch.float32, device=dev)
-        _check_out(payload, "payload", torch.uint8, T * pw)
-        _check_out(scales, "scales", torch.uint8, total)
+        _check_out(payload, "payload", torch.uint8, T * pw, dev)
+        _check_out(scales, "scales", torch.uint8, total, dev)
         if row_amax is not None:
-            _check_out(row_amax, "row_amax", torch.float32, T)
+            _check_out(row_amax, "row_amax", torch.float32, T, dev)
         if mode == "nvfp4":
             if global_scale is None:
                 raise ValueError("nvfp4 split needs global_scale")
@@ -408,10 +414,14 @@ class FusedCall:
             raise ValueError("x, residual: contiguous [T, H]; gamma: contiguous [H]")
         T, H = x.shape
         dev = x.device
+        if residual.device != dev or gamma.device != dev:
+            raise ValueError("x, residual and gamma must be on one device")
         if fmt == NVFP4:
             if global_scale is None:
                 raise ValueError("NVFP4 needs global_scale")
             _need_gpu(global_scale, "global_scale", torch.float32)
+            if global_scale.device != dev:
+                raise ValueError(f"global_scale must be on {dev}")
         pw = H if fmt == MXFP8 else H // 2
         nb = lib().mxq_scale_bytes(T, H, fmt, layout)
         if nb < 0:
@@ -421,10 +431,10 @@ class FusedCall:
                    torch.empty((T, pw), dtype=torch.uint8, device=dev),
                    torch.empty(nb, dtype=torch.uint8, device=dev))
         res_out, norm_out, payload, scales = out
-        _check_out(res_out, "residual_out", torch.bfloat16, T * H)
-        _check_out(norm_out, "norm_out", torch.bfloat16, T * H)
-        _check_out(payload, "payload", torch.uint8, T * pw)
-        _check_out(scales, "scales", torch.uint8, nb)
+        _check_out(res_out, "residual_out", torch.bfloat16, T * H, dev)
+        _check_out(norm_out, "norm_out", torch.bfloat16, T * H, dev)
+        _check_out(payload, "payload", torch.uint8, T * pw, dev)
+        _check_out(scales, "scales", torch.uint8, nb, dev)
         self.device = dev
         self.keep = (x, residual, gamma, global_scale)
         self.out = (res_out, norm_out, payload, scales)
@@ -456,7 +466,7 @@ def scale_swizzle(linear: torch.Tensor, out: Optional[torch.Tensor] = None) -> t
     n = (-(-rows // 128) * 128) * (-(-C // 4) * 4)
     if out is None:
         out = torch.empty(n, dtype=torch.uint8, device=linear.device)
-    _check_out(out, "out", torch.uint8, n)
+    _check_out(out, "out", torch.uint8, n, linear.device)
     rc = lib().scale_swizzle(linear.data_ptr(), rows, C, out.data_ptr(), _stream(linear.device))
     _check(rc, "scale_swizzle")
     return out

@@ -238,3 +238,14 @@ def test_binding_rejects_small_outputs():
         mxq.scale_swizzle(torch.zeros(64, 8, dtype=torch.uint8, device=DEV), small)
     with pytest.raises(ValueError):
         mxq.mx_quant_grouped(mxq.MXFP8, mxq.LINEAR, [x], payloads=[small])
+    # encode-scale outputs: too small, not contiguous; no sources at all
+    with pytest.raises(ValueError):
+        mxq.nvfp4_quant_grouped_auto(mxq.SWIZZLED, [x, x], g_out=torch.empty(1, device=DEV))
+    with pytest.raises(ValueError):
+        mxq.nvfp4_quant_grouped_auto(mxq.SWIZZLED, [x, x],
+                                     amax_out=torch.empty(4, device=DEV)[::2])
+    with pytest.raises(ValueError):
+        mxq.nvfp4_quant_grouped_auto(mxq.SWIZZLED, [])
+    # outputs on the host
+    with pytest.raises(ValueError):
+        mxq.mxfp8_quant_split(x, [64], mxq.LINEAR, payload=torch.empty(64 * 256, dtype=torch.uint8))
