@@ -129,17 +129,28 @@ def set_max_workgroups(n: int) -> None:
     lib().mxq_set_max_workgroups(int(n))
 
 
+def _per_launch(max_per_launch) -> int:
+    """The per-call expert cap: 1..MAX_GROUP; 1 is the one-launch-per-expert path."""
+    n = int(max_per_launch)
+    if n < 1 or n > MAX_GROUP:
+        raise ValueError(f"max_per_launch must be in 1..{MAX_GROUP}, got {n}")
+    return n
+
+
 def mx_quant_grouped(fmt: int, layout: int, srcs: Sequence[torch.Tensor],
                      payloads: Optional[Sequence[torch.Tensor]] = None,
                      scales: Optional[Sequence[torch.Tensor]] = None,
-                     global_scales: Optional[torch.Tensor] = None):
-    """Quantize same-width bf16 expert tensors, MAX_GROUP per launch.
+                     global_scales: Optional[torch.Tensor] = None,
+                     max_per_launch: int = MAX_GROUP):
+    """Quantize same-width bf16 expert tensors, max_per_launch (1..16) per launch.
 
     srcs: 2-D bf16 GPU tensors [rows_i, cols] with unit column stride.
     global_scales: NVFP4 only, fp32 GPU tensor [len(srcs)] of encode scales.
     Returns (payloads, scales) lists of uint8 tensors (allocated when None):
     payload [rows, cols] (MXFP8) or [rows, cols/2] (NVFP4); scales flat,
-    scale_bytes(rows, cols, fmt, layout) bytes."""
+    scale_bytes(rows, cols, fmt, layout) bytes.  The bytes do not depend on
+    max_per_launch."""
+    per = _per_launch(max_per_launch)
     srcs = list(srcs)
     if not srcs:
         return [], []
@@ -147,8 +158,8 @@ def mx_quant_grouped(fmt: int, layout: int, srcs: Sequence[torch.Tensor],
     cols = srcs[0].shape[1]
     dev = srcs[0].device
     stream = _stream(dev)
-    for b in range(0, len(srcs), MAX_GROUP):
-        n = min(MAX_GROUP, len(srcs) - b)
+    for b in range(0, len(srcs), per):
+        n = min(per, len(srcs) - b)
         ents = (_Entry * n)()
         for j in range(n):
             i = b + j
@@ -165,10 +176,13 @@ class GroupedCall:
 
     For callers that issue the same grouped quantization repeatedly (a refit
     loop, a benchmark): the tensors are checked and the C descriptor arrays
-    packed at construction; each call is one C call per 16 experts on the
-    current stream.  The tensors must stay alive and keep their storage."""
+    packed at construction; each call is one C call per max_per_launch
+    (default 16) experts on the current stream.  The tensors must stay alive
+    and keep their storage."""
 
-    def __init__(self, fmt, layout, srcs, payloads=None, scales=None, global_scales=None):
+    def __init__(self, fmt, layout, srcs, payloads=None, scales=None, global_scales=None,
+                 max_per_launch=MAX_GROUP):
+        per = _per_launch(max_per_launch)
         self.fmt, self.layout = fmt, layout
         self.payloads, self.scales = _grouped_outputs(fmt, layout, srcs, payloads, scales,
                                                       global_scales)
@@ -177,8 +191,8 @@ class GroupedCall:
         self.cols = self.srcs[0].shape[1]
         self.device = self.srcs[0].device
         self._batches = []
-        for b in range(0, len(self.srcs), MAX_GROUP):
-            n = min(MAX_GROUP, len(self.srcs) - b)
+        for b in range(0, len(self.srcs), per):
+            n = min(per, len(self.srcs) - b)
             ents = (_Entry * n)()
             for j in range(n):
                 i = b + j

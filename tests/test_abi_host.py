@@ -247,3 +247,14 @@ def test_header_compiles_as_c99_and_links(tmp_path):
     p = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
     assert p.returncode == 0, p.stdout + p.stderr
     assert "ok: 0 failed" in p.stdout
+
+
+def test_binding_per_call_cap():
+    """The per-call expert cap: values outside 1..16 raise before any tensor is
+    looked at (0 and negatives included); 1 is the one-launch-per-expert path."""
+    for bad in (0, -1, 17):
+        with pytest.raises(ValueError):
+            mxq.mx_quant_grouped(0, 0, [], max_per_launch=bad)
+        with pytest.raises(ValueError):
+            mxq.GroupedCall(0, 0, [], max_per_launch=bad)
+    assert mxq.mx_quant_grouped(0, 0, [], max_per_launch=1) == ([], [])

@@ -169,6 +169,24 @@ def test_batched_equals_per_expert_16_and_17(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+def test_per_call_cap_keeps_bytes(fmt):
+    """The binding's per-call cap (1, 5 or 16 experts per launch) changes the
+    launches, never the bytes."""
+    xs = [x.to(DEV) for x in workloads.small_grouped_experts(n_experts=11, rows=96, cols=512,
+                                                             seed=11)]
+    gs = torch.cat([g_of(x) for x in xs]) if fmt == 1 else None
+    say("per-call cap", fmt)
+    ref = None
+    for cap in (16, 5, 1):
+        pays, scs = mxq.mx_quant_grouped(fmt, mxq.LINEAR, xs, global_scales=gs,
+                                         max_per_launch=cap)
+        got = [u8(t) for t in pays + scs]
+        if ref is None:
+            ref = got
+        assert all(np.array_equal(a, b) for a, b in zip(got, ref)), cap
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_qwen3_30b_layer_shapes(orc, fmt):
     """Qwen3-30B-A3B layer shapes, 16 experts per launch (one launch per
     projection here), swizzled scales, byte-exact on every expert."""
