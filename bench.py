@@ -150,7 +150,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the grouped quantization shards by expert with no exchange; "
               "run it per GPU with --gpus 1)", file=sys.stderr)
         sys.exit(2)

@@ -65,7 +65,7 @@ typedef enum {
     MXQ_OK = 0,
     MXQ_EINVAL = 1,       /* null pointer, bad enum, bad count or split, bad eps       */
     MXQ_ESHAPE = 2,       /* cols not a multiple of the block, misaligned pointer ... */
-    MXQ_EUNSUPPORTED = 3, /* a combination this build does not implement            */
+    MXQ_EUNSUPPORTED = 3, /* a combination the library does not implement           */
     MXQ_ELAUNCH = 4       /* the HIP runtime rejected a kernel launch                 */
 } mxq_status;
 
