@@ -466,6 +466,15 @@ def extra_workloads(torch, mxq, workloads, dev):
     t = timed(torch, lambda i: call(), 100)
     res["small_grouped_8x256x512_mxfp8"] = {"us": round(t * 1e6, 2),
                                             "GBps": round(3178496 / t / 1e9, 1)}
+
+    # receiver-side scale conversion: the linear MXFP8 scales of one 16-expert
+    # gate_up launch (16 x [3072, 128] stacked) to the swizzled layout
+    lin = [torch.randint(0, 255, (16 * 3072, 128), dtype=torch.uint8, device=dev)
+           for _ in range(4)]
+    outs = [torch.empty(16 * 3072 * 128, dtype=torch.uint8, device=dev) for _ in range(4)]
+    t = timed(torch, lambda i: mxq.scale_swizzle(lin[i % 4], outs[i % 4]), 50)
+    nb = 2 * 16 * 3072 * 128
+    res["scale_swizzle_49152x128"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
     return res
 
 

@@ -153,29 +153,49 @@ void k_fused(const FusedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Linear -> swizzled scale layout.  One thread per 16-byte output vector:
-// rows 32*q + i (q = 0..3) of a 128-row band, 4 columns each; padding is 0.
+// Linear -> swizzled scale layout.  A unit is one 128-row band by
+// 4 * kSwizzleTiles scale columns: its linear codes are read row by row into LDS (coalesced),
+// then its tiles leave as one contiguous run of 16-byte lines.  Rows and
+// columns past the matrix read as 0, which is the padding.
 // ---------------------------------------------------------------------------
+constexpr int kSwzWords = kSwizzleTiles;  // words (4 codes) per unit row
+
 __global__ __launch_bounds__(kThreads) void k_swizzle(const SwizzleArgs a) {
-    for (int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x; k < a.n_vec;
-         k += (int64_t)gridDim.x * kThreads) {
-        const int64_t tile = k >> 5;
-        const int i = (int)(k & 31);
-        const int64_t band = tile / a.tiles_per_band;
-        const int64_t c0 = (tile % a.tiles_per_band) * 4;
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t r = band * 128 + 32 * q + i;
+    // the unit's 128 rows x kSwzCols codes, one word (4 codes of a tile) per
+    // entry; the odd row pitch keeps the column reads on distinct banks
+    __shared__ uint32_t codes[128][kSwzWords + 1];
+    // rows of a multiple of 4 codes from a 4-byte aligned base: each row's 4
+    // codes of a tile are one aligned word (the usual case; uniform)
+    const bool words = (a.cols & 3) == 0 && (reinterpret_cast<uintptr_t>(a.lin) & 3) == 0;
+    const int64_t groups = (a.tiles_per_band + kSwzWords - 1) / kSwzWords;
+    const int64_t n_units = (a.rows + 127) / 128 * groups;
+    for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
+        const int64_t band = u / groups, t0 = (u - band * groups) * kSwzWords;
+        for (int k = threadIdx.x; k < 128 * kSwzWords; k += kThreads) {
+            const int row = k / kSwzWords, wc = k - row * kSwzWords;
+            const int64_t r = band * 128 + row, c0 = (t0 + wc) * 4;
             uint32_t word = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t c = c0 + j;
-                if (r < a.rows && c < a.cols) word |= (uint32_t)a.lin[r * a.cols + c] << (8 * j);
+            if (r < a.rows && c0 < a.cols) {
+                if (words) {
+                    word = *reinterpret_cast<const uint32_t *>(a.lin + r * a.cols + c0);
+                } else {
+                    for (int j = 0; j < 4 && c0 + j < a.cols; ++j)
+                        word |= (uint32_t)a.lin[r * a.cols + c0 + j] << (8 * j);
+                }
             }
-            w[q] = word;
+            codes[row][wc] = word;
         }
-        *reinterpret_cast<u32x4 *>(a.swz + k * 16) = u32x4{w[0], w[1], w[2], w[3]};
+        __syncthreads();
+        // the unit's tiles are contiguous in the output: 512 bytes each, 16
+        // bytes per line p holding rows p, p+32, p+64, p+96
+        const int n_t = (int)min((int64_t)kSwzWords, a.tiles_per_band - t0);
+        uint8_t *dst = a.swz + (band * a.tiles_per_band + t0) * 512;
+        for (int k = threadIdx.x; k < n_t * 32; k += kThreads) {
+            const int t = k >> 5, p = k & 31;
+            *reinterpret_cast<u32x4 *>(dst + k * 16) =
+                u32x4{codes[p][t], codes[p + 32][t], codes[p + 64][t], codes[p + 96][t]};
+        }
+        __syncthreads();
     }
 }
 

@@ -107,13 +107,18 @@ struct FusedArgs {
 // 1-4 us faster.
 constexpr int64_t kFusedFourWaveMaxT = 1536;
 
+#ifndef MXQ_SWZ_TILES
+#define MXQ_SWZ_TILES 16
+#endif
+// Scale swizzle unit: one 128-row band by this many 4-column tiles.
+constexpr int kSwizzleTiles = MXQ_SWZ_TILES;
+
 struct SwizzleArgs {
     const uint8_t *lin;
     uint8_t *swz;
     int64_t rows;
     int64_t cols;        // scale columns C
     int64_t tiles_per_band;  // round_up(C, 4) / 4
-    int64_t n_vec;       // 16-byte output vectors
 };
 
 // Launchers: return hipSuccess or the launch error.
