@@ -321,8 +321,9 @@ int scale_swizzle(const void *linear, int64_t rows, int64_t sf_cols, void *swizz
     a.rows = rows;
     a.cols = sf_cols;
     a.tiles_per_band = round_up(sf_cols, 4) / 4;
-    // units: 128-row bands x groups of kSwizzleTiles tiles
-    int64_t grid = (rows + 127) / 128 * ((a.tiles_per_band + kSwizzleTiles - 1) / kSwizzleTiles);
+    a.unit_tiles = (int32_t)(a.tiles_per_band < kSwizzleTiles ? a.tiles_per_band : kSwizzleTiles);
+    // units: 128-row bands x groups of unit_tiles tiles
+    int64_t grid = (rows + 127) / 128 * ((a.tiles_per_band + a.unit_tiles - 1) / a.unit_tiles);
     if (grid > 65536) grid = 65536;
     hipError_t err = launch_swizzle(a, grid_for(grid), (hipStream_t)stream);
     return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;

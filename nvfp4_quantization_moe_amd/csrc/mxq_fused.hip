@@ -153,47 +153,59 @@ void k_fused(const FusedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Linear -> swizzled scale layout.  A unit is one 128-row band by
-// 4 * kSwizzleTiles scale columns: its linear codes are read row by row into LDS (coalesced),
-// then its tiles leave as one contiguous run of 16-byte lines.  Rows and
-// columns past the matrix read as 0, which is the padding.
+// Linear -> swizzled scale layout.  A unit is one 128-row band by up to
+// kSwizzleTiles tiles (4 scale columns each): its linear codes are read row
+// by row into LDS, then its tiles leave as one contiguous run of 16-byte
+// lines.  Rows and columns past the matrix read as 0, which is the padding.
 // ---------------------------------------------------------------------------
-constexpr int kSwzWords = kSwizzleTiles;  // words (4 codes) per unit row
-
 __global__ __launch_bounds__(kThreads) void k_swizzle(const SwizzleArgs a) {
-    // the unit's 128 rows x kSwzCols codes, one word (4 codes of a tile) per
-    // entry; the odd row pitch keeps the column reads on distinct banks
-    __shared__ uint32_t codes[128][kSwzWords + 1];
+    // the unit's 128 rows x (4 * nt) codes, one word (4 codes of a tile) per
+    // entry; the odd row pitch nt + 1 keeps the column reads on distinct banks
+    extern __shared__ uint32_t codes[];
+    const int nt = a.unit_tiles, pitch = nt + 1;
     // rows of a multiple of 4 codes from a 4-byte aligned base: each row's 4
     // codes of a tile are one aligned word (the usual case; uniform)
     const bool words = (a.cols & 3) == 0 && (reinterpret_cast<uintptr_t>(a.lin) & 3) == 0;
-    const int64_t groups = (a.tiles_per_band + kSwzWords - 1) / kSwzWords;
+    const int64_t groups = (a.tiles_per_band + nt - 1) / nt;
     const int64_t n_units = (a.rows + 127) / 128 * groups;
     for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
-        const int64_t band = u / groups, t0 = (u - band * groups) * kSwzWords;
-        for (int k = threadIdx.x; k < 128 * kSwzWords; k += kThreads) {
-            const int row = k / kSwzWords, wc = k - row * kSwzWords;
-            const int64_t r = band * 128 + row, c0 = (t0 + wc) * 4;
-            uint32_t word = 0;
-            if (r < a.rows && c0 < a.cols) {
-                if (words) {
-                    word = *reinterpret_cast<const uint32_t *>(a.lin + r * a.cols + c0);
-                } else {
-                    for (int j = 0; j < 4 && c0 + j < a.cols; ++j)
-                        word |= (uint32_t)a.lin[r * a.cols + c0 + j] << (8 * j);
+        const int64_t band = u / groups, t0 = (u - band * groups) * nt;
+        // kBatch loads in flight per thread before any LDS write
+        constexpr int kBatch = 8;
+        for (int k0 = 0; k0 < 128 * nt; k0 += kBatch * kThreads) {
+            uint32_t w[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int k = k0 + b * kThreads + (int)threadIdx.x;
+                const int row = k / nt, wc = k - row * nt;
+                const int64_t r = band * 128 + row, c0 = (t0 + wc) * 4;
+                w[b] = 0;
+                if (k < 128 * nt && r < a.rows && c0 < a.cols) {
+                    if (words) {
+                        w[b] = *reinterpret_cast<const uint32_t *>(a.lin + r * a.cols + c0);
+                    } else {
+                        for (int j = 0; j < 4 && c0 + j < a.cols; ++j)
+                            w[b] |= (uint32_t)a.lin[r * a.cols + c0 + j] << (8 * j);
+                    }
                 }
             }
-            codes[row][wc] = word;
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int k = k0 + b * kThreads + (int)threadIdx.x;
+                const int row = k / nt;
+                if (k < 128 * nt) codes[row * pitch + (k - row * nt)] = w[b];
+            }
         }
         __syncthreads();
         // the unit's tiles are contiguous in the output: 512 bytes each, 16
         // bytes per line p holding rows p, p+32, p+64, p+96
-        const int n_t = (int)min((int64_t)kSwzWords, a.tiles_per_band - t0);
+        const int n_t = (int)min((int64_t)nt, a.tiles_per_band - t0);
         uint8_t *dst = a.swz + (band * a.tiles_per_band + t0) * 512;
         for (int k = threadIdx.x; k < n_t * 32; k += kThreads) {
             const int t = k >> 5, p = k & 31;
             *reinterpret_cast<u32x4 *>(dst + k * 16) =
-                u32x4{codes[p][t], codes[p + 32][t], codes[p + 64][t], codes[p + 96][t]};
+                u32x4{codes[p * pitch + t], codes[(p + 32) * pitch + t],
+                      codes[(p + 64) * pitch + t], codes[(p + 96) * pitch + t]};
         }
         __syncthreads();
     }
@@ -253,7 +265,8 @@ hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, h
 }
 
 hipError_t launch_swizzle(const SwizzleArgs &a, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL(k_swizzle, dim3(grid_of(grid)), dim3(kThreads), 0, s, a);
+    const size_t lds = (size_t)128 * (a.unit_tiles + 1) * 4;  // 8.5 KiB at 16 tiles
+    hipLaunchKernelGGL(k_swizzle, dim3(grid_of(grid)), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 

@@ -107,11 +107,11 @@ struct FusedArgs {
 // 1-4 us faster.
 constexpr int64_t kFusedFourWaveMaxT = 1536;
 
-#ifndef MXQ_SWZ_TILES
-#define MXQ_SWZ_TILES 16
-#endif
-// Scale swizzle unit: one 128-row band by this many 4-column tiles.
-constexpr int kSwizzleTiles = MXQ_SWZ_TILES;
+// Scale swizzle unit: one 128-row band by at most this many 4-column tiles.
+// Wider units (whole rows up to 512 columns) leave too few workgroups, each
+// with more serial loads: 16 / 32 / 64 / 128 tiles took 9.0 / 9.5 / 11.9 /
+// 16.6 us on a [31488, 448] matrix.
+constexpr int kSwizzleTiles = 16;
 
 struct SwizzleArgs {
     const uint8_t *lin;
@@ -119,6 +119,8 @@ struct SwizzleArgs {
     int64_t rows;
     int64_t cols;        // scale columns C
     int64_t tiles_per_band;  // round_up(C, 4) / 4
+    int32_t unit_tiles;  // tiles per unit: min(tiles_per_band, kSwizzleTiles)
+    int32_t pad_;
 };
 
 // Launchers: return hipSuccess or the launch error.
