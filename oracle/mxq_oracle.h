@@ -28,9 +28,10 @@
  * fixes an fp32 operation; each such operation is written as a C float
  * operation (IEEE-754 binary32, round-to-nearest-even, no contraction).
  *
- * Parity-unpinned readings (the pages do not fix them; see the design notes):
- *   - the 128x4 swizzle permutation, the E2M1 nibble order, the NVFP4
- *     arithmetic order and the meaning of the global scale are fixed by fiat.
+ * Readings the pages leave open: the 128x4 swizzle permutation, the E2M1
+ * nibble order, the NVFP4 arithmetic order and the encode-scale formula.  Each
+ * is taken as stated at its function and pinned by hand-derived fixtures
+ * (tests/golden/), so no function here is left without a pin.
  */
 #ifndef MXQ_ORACLE_H
 #define MXQ_ORACLE_H
