@@ -166,7 +166,7 @@ def mx_quant_grouped(fmt: int, layout: int, srcs: Sequence[torch.Tensor],
             s = srcs[i]
             gs = None if fmt == MXFP8 else global_scales.data_ptr() + 4 * i
             ents[j] = _Entry(s.data_ptr(), payloads[i].data_ptr(), scales[i].data_ptr(), gs,
-                             s.shape[0], s.stride(0))
+                             s.shape[0], _row_stride(s))
         _check(lib().mx_quant_grouped(fmt, layout, cols, ents, n, stream), "mx_quant_grouped")
     return payloads, scales
 
@@ -199,7 +199,7 @@ class GroupedCall:
                 s = self.srcs[i]
                 gs = None if fmt == MXFP8 else global_scales.data_ptr() + 4 * i
                 ents[j] = _Entry(s.data_ptr(), self.payloads[i].data_ptr(),
-                                 self.scales[i].data_ptr(), gs, s.shape[0], s.stride(0))
+                                 self.scales[i].data_ptr(), gs, s.shape[0], _row_stride(s))
             self._batches.append((ents, n))
 
     def __call__(self, stream: Optional[ctypes.c_void_p] = None):
@@ -253,7 +253,7 @@ class GroupedAutoCall:
                 i = b + j
                 x = self.srcs[i]
                 ents[j] = _Entry(x.data_ptr(), self.payloads[i].data_ptr(),
-                                 self.scales[i].data_ptr(), None, x.shape[0], x.stride(0))
+                                 self.scales[i].data_ptr(), None, x.shape[0], _row_stride(x))
             if slots is not None:
                 sl, ns, off = (ctypes.c_int * m)(*slots), n_slots, 0
             else:
@@ -283,7 +283,9 @@ def _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales):
     dev = srcs[0].device
     for i, s in enumerate(srcs):
         _need_gpu(s, f"srcs[{i}]", torch.bfloat16)
-        if s.dim() != 2 or s.stride(1) != 1 or s.shape[1] != cols or s.device != dev:
+        # an empty tensor holds no data: its strides (possibly 0) are not checked
+        if s.dim() != 2 or s.shape[1] != cols or s.device != dev or \
+                (s.shape[0] > 0 and s.stride(1) != 1):
             raise ValueError(f"srcs[{i}]: expected a row-major [rows, {cols}] bf16 tensor on {dev}")
     if fmt == NVFP4:
         if global_scales is None:
@@ -308,6 +310,11 @@ def _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales):
         if c.numel() < scale_bytes(s.shape[0], cols, fmt, layout) or not c.is_contiguous():
             raise ValueError(f"scales[{i}] too small or not contiguous")
     return payloads, scales
+
+
+def _row_stride(s: torch.Tensor) -> int:
+    """Row stride in elements for the descriptor; an empty tensor's is its width."""
+    return s.stride(0) if s.shape[0] > 0 else s.shape[1]
 
 
 def _check_out(t, name, dtype, numel, dev):

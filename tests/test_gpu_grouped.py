@@ -126,6 +126,26 @@ def test_widest_rows(orc, fmt, layout):
             assert np.array_equal(scs[i], s), (cols, i)
 
 
+def test_empty_expert_with_zero_strides(orc):
+    """A zero-row expert whose strides are (0, 0) (an empty array from numpy)
+    is accepted among ordinary experts and changes none of their bytes."""
+    empty = torch.from_numpy(np.zeros((0, 256), np.int16)).view(torch.bfloat16).to(DEV)
+    assert empty.stride() == (0, 0) or empty.shape[0] == 0
+    xs_cpu = [(torch.randn(r, 256) * 3).to(torch.bfloat16) for r in (70, 1)]
+    xs = [xs_cpu[0].to(DEV), empty, xs_cpu[1].to(DEV)]
+    gs = torch.cat([g_of(xs[0]), torch.ones(1, device=DEV), g_of(xs[2])])
+    say("empty expert, zero strides")
+    for fmt in (0, 1):
+        pays, scs = run_grouped(fmt, mxq.SWIZZLED, xs, gs if fmt == 1 else None)
+        assert pays[1].size == 0 and scs[1].size == 0
+        for i, x in ((0, xs_cpu[0]), (2, xs_cpu[1])):
+            p, s = oracle_entry(orc, fmt, orc.SWIZZLED, x, float(gs[i]) if fmt == 1 else 1.0)
+            assert np.array_equal(pays[i], p.ravel()) and np.array_equal(scs[i], s), (fmt, i)
+    pays, scs, g, am = mxq.nvfp4_quant_grouped_auto(mxq.SWIZZLED, xs)
+    torch.cuda.synchronize()
+    assert float(am[1]) == 0.0 and float(g[1]) == 1.0
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_strided_source_rows(orc, fmt):
     say("strided src", fmt)

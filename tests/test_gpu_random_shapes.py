@@ -15,7 +15,7 @@ from gpu_common import say, u8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 24
+N_CASES = 48
 
 
 def _values(gen, rows, cols):
@@ -117,7 +117,7 @@ def test_random_fused(orc, case):
     assert np.array_equal(u8(p), op.ravel()) and np.array_equal(u8(s), os_)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_random_auto_scale(orc, case):
     gen = torch.Generator().manual_seed(4000 + case)
     layout = int(torch.randint(0, 2, (1,), generator=gen))
