@@ -217,6 +217,25 @@ def test_fused_grid_invariance(orc, fmt):
         mxq.set_max_workgroups(0)
 
 
+def test_empty_activations_through_the_binding():
+    """T = 0 through every split form and the fused call: outputs are empty,
+    nothing is launched, and no error is raised (a zero-row array from numpy
+    has strides (0, 0); the binding must not care)."""
+    for H in (256, 7168):
+        x = torch.from_numpy(np.zeros((0, H), np.int16)).view(torch.bfloat16).to(DEV)
+        g = torch.ones(1, dtype=torch.float32, device=DEV)
+        say("empty activation", H)
+        for p, s, a in (mxq.nvfp4_quant_split(x, [0, 0], g, mxq.SWIZZLED),
+                        mxq.nvfp4_quant_split_row_scaled(x, [0], mxq.LINEAR),
+                        mxq.mxfp8_quant_split(x, [0, 0, 0], mxq.SWIZZLED)):
+            assert p.numel() == 0 and s.numel() == 0 and a.numel() == 0
+        gm = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+        for fmt in (0, 1):
+            ro, no, p, s = mxq.rmsnorm_quant_fused(x, x, gm, 1e-6, fmt, mxq.SWIZZLED, g)
+            assert ro.numel() == no.numel() == p.numel() == s.numel() == 0
+    torch.cuda.synchronize()
+
+
 def test_binding_rejects_small_outputs():
     """Outputs smaller than the call writes are refused before any launch."""
     x = torch.zeros(64, 256, dtype=torch.bfloat16, device=DEV)
