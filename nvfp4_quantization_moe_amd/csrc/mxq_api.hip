@@ -301,8 +301,10 @@ int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual
     a.H = (int32_t)H;
     a.sf_cols = (int32_t)C;
     a.sf_stride = (int32_t)(layout == MXQ_SF_SWIZZLED ? round_up(C, 4) : C);
-    a.wpr = T <= kFusedFourWaveMaxT ? 4 : 2;
-    a.rpu = a.wpr == 4 ? 1 : 4;
+    const int64_t wide_max =
+        layout == MXQ_SF_SWIZZLED ? kFusedWideMaxTSwizzled : kFusedWideMaxTLinear;
+    a.wpr = T <= wide_max ? 16 : T <= kFusedFourWaveMaxT ? 4 : 2;
+    a.rpu = a.wpr == 2 ? 4 : 1;
     const int64_t units = row_groups(T, layout, a.rpu);
     a.total_units = (int32_t)units;
     hipError_t err = launch_fused(fmt, layout, a, grid_for(units), (hipStream_t)stream);

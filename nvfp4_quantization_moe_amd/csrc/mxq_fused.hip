@@ -236,15 +236,17 @@ static void fused_nch(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
     }
 }
 
-// The shape is the host's choice (a.wpr, a.rpu): four waves per row and
-// one-row units for latency-bound calls (short per-row chains, many
-// workgroups), two waves per row and four-row units for large ones.  Units
-// of rows 32 apart (whole 16-byte swizzled pieces per unit) measured 3-6 %
-// slower at T = 4096 than these consecutive rows.
+// The shape is the host's choice (a.wpr, a.rpu): sixteen or four waves per
+// row and one-row units for latency-bound calls (the more waves, the shorter
+// each row's chain of dependent loads), two waves per row and four-row units
+// for large ones.  Units of rows 32 apart (whole 16-byte swizzled pieces per
+// unit) measured 3-6 % slower at T = 4096 than these consecutive rows.
 template <int FMT, int LAYOUT>
 static void fused_wpr(const FusedArgs &a, dim3 gd, size_t lds, hipStream_t s) {
     if (a.wpr == 2)
         fused_nch<FMT, LAYOUT, 2, 4>(a, gd, lds, s);
+    else if (a.wpr == 16)
+        fused_nch<FMT, LAYOUT, 16, 1>(a, gd, lds, s);
     else
         fused_nch<FMT, LAYOUT, 4, 1>(a, gd, lds, s);
 }

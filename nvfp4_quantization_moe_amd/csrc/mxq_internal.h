@@ -96,15 +96,21 @@ struct FusedArgs {
     int32_t sf_cols;
     int32_t sf_stride;
     int32_t total_units;
-    int32_t wpr;          // waves per row: 4 (with rpu 1) or 2 (with rpu 4)
+    int32_t wpr;          // waves per row: 16 or 4 (with rpu 1), or 2 (with rpu 4)
     int32_t rpu;          // rows per unit
 };
 
-// Fused epilogue shape for T rows: up to this many rows, four waves per row
-// and one-row units (latency bound: short per-row chains, many workgroups);
-// beyond, two waves per row and four-row units (bandwidth bound).  At
-// H = 7168 the two shapes tie near T = 1536; at T = 2048 four-row units are
-// 1-4 us faster.
+// Fused epilogue shape for T rows (measured at H = 7168):
+//  * up to kFusedWideMaxT rows, sixteen waves per row and one-row units: each
+//    wave loads one 512-column step, so a row's loads are all in flight at
+//    once (T = 1 / 256: 3.8-4.3 / 4.9-5.4 us against 4.9-6.2 / 6.6-7.8 with
+//    four waves); with linear scales the edge comes earlier (T = 384: 8.9
+//    against 8.0 us);
+//  * up to kFusedFourWaveMaxT rows, four waves per row and one-row units;
+//  * beyond, two waves per row and four-row units (bandwidth bound).  The
+//    last two tie near T = 1536; at T = 2048 four-row units are 1-4 us faster.
+constexpr int64_t kFusedWideMaxTSwizzled = 512;
+constexpr int64_t kFusedWideMaxTLinear = 256;
 constexpr int64_t kFusedFourWaveMaxT = 1536;
 
 // Scale swizzle unit: one 128-row band by at most this many 4-column tiles.

@@ -198,9 +198,10 @@ def _fused_check(orc, T, H, fmt, layout, seed, eps=1e-6, g=37.5):
 @pytest.mark.parametrize("layout", [0, 1])
 def test_fused_widths_both_row_splits(orc, fmt, layout):
     """Row widths with ragged 512-column tails, up to the 16384 maximum, on
-    both sides of the launcher's switch from four to two waves per row."""
-    for T, H in ((5, 128), (5, 640), (3, 16384), (130, 2176), (1536, 640), (2100, 640),
-                 (1537, 2176)):
+    both sides of the launcher's switches from sixteen to four waves per row
+    (T = 256 linear, 512 swizzled) and from four to two (T = 1536)."""
+    for T, H in ((5, 128), (5, 640), (3, 16384), (130, 2176), (256, 640), (257, 2176),
+                 (512, 640), (513, 16384), (1536, 640), (2100, 640), (1537, 2176)):
         say("fused widths, fmt", fmt, "layout", layout, "T", T, "H", H)
         _fused_check(orc, T, H, fmt, layout, seed=T + H)
 
