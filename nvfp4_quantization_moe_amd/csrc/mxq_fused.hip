@@ -1,10 +1,10 @@
 // mxq_fused.hip -- the fused residual add + RMSNorm + quantize epilogue, and
 // the linear -> swizzled scale conversion.
 //
-// The epilogue needs whole rows (the RMSNorm sum of squares): two or four
-// waves own one row and hold it in registers.  A unit is RPU consecutive
-// rows; swizzled units cover the padding rows up to the next multiple of 128
-// too.  Every byte has one writer.
+// The epilogue needs whole rows (the RMSNorm sum of squares): two, four or
+// sixteen waves own one row and hold it in registers.  A unit is RPU
+// consecutive rows; swizzled units cover the padding rows up to the next
+// multiple of 128 too.  Every byte has one writer.
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
