@@ -149,7 +149,8 @@ int nvfp4_quant_grouped_auto(int layout, int64_t cols, const mxq_entry *entries,
  *                expert owns no bytes (16-byte aligned base if swizzled)
  *   row_amax     device fp32 [total_rows]: max_j |src[r, j]| (NULL to skip)
  * cols is a multiple of 16, at most 16384.  Any number of splits is allowed.
- * total_rows == 0 is MXQ_OK with no launch.
+ * 0 <= total_rows < 2^31, else MXQ_EINVAL; total_rows == 0 is MXQ_OK with no
+ * launch.
  */
 int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols,
                       const int64_t *split_rows, int n_splits, const float *global_scale,
