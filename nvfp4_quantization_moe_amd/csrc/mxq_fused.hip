@@ -168,7 +168,12 @@ __global__ __launch_bounds__(kThreads) void k_swizzle(const SwizzleArgs a) {
     const bool words = (a.cols & 3) == 0 && (reinterpret_cast<uintptr_t>(a.lin) & 3) == 0;
     const int64_t groups = (a.tiles_per_band + nt - 1) / nt;
     const int64_t n_units = (a.rows + 127) / 128 * groups;
-    for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
+    // the units of one band (up to 16) run on one XCD: each 128-byte line of
+    // the band's rows is read by several of them, and one L2 then fetches it
+    // once (measured 2.0x -> 1.02x the input on 128-column rows)
+    const int g = groups < 16 ? (int)groups : 16;
+    for (int64_t u0 = blockIdx.x; u0 < n_units; u0 += gridDim.x) {
+        const int64_t u = (int64_t)gridDim.x == n_units ? xcd_grouped_unit(u0, n_units, g) : u0;
         const int64_t band = u / groups, t0 = (u - band * groups) * nt;
         // kBatch loads in flight per thread before any LDS write
         constexpr int kBatch = 8;

@@ -28,6 +28,13 @@ __device__ __forceinline__ int xcd_grouped_unit(int b, int n) {
     return b / kBlock * kBlock + (b & 7) * G + (b >> 3) % G;
 }
 
+// The same with a group size g known only at run time (g >= 1).
+__device__ __forceinline__ int64_t xcd_grouped_unit(int64_t b, int64_t n, int g) {
+    const int64_t block = (int64_t)g * 8;
+    if (b >= n / block * block) return b;
+    return b / block * block + (b & 7) * g + (b >> 3) % g;
+}
+
 // One grouped-launch descriptor.  The whole table travels in the kernel
 // arguments, so a grouped call is one dispatch with no device-side table.
 struct GEntry {
