@@ -135,3 +135,17 @@ def test_random_auto_scale(orc, case):
     assert np.array_equal(am[:k].cpu().numpy(), oa) and np.array_equal(g[:k].cpu().numpy(), og)
     for i in range(n):
         assert np.array_equal(u8(pays[i]), op[i].ravel()) and np.array_equal(u8(scs[i]), os_[i])
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_swizzle(orc, case):
+    """scale_swizzle on random [rows, cols] matrices: ragged bands, any column
+    count (word and byte loads), one to many 16-tile units per band."""
+    gen = torch.Generator().manual_seed(5000 + case)
+    rows = int(torch.randint(0, 3000, (1,), generator=gen))
+    cols = int(torch.randint(1, 700, (1,), generator=gen))
+    lin = torch.randint(0, 256, (rows, cols), generator=gen, dtype=torch.int32).to(torch.uint8)
+    say("random swizzle", case, "rows", rows, "cols", cols)
+    got = mxq.scale_swizzle(lin.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(got), orc.scale_swizzle(lin.numpy()))
