@@ -70,7 +70,7 @@ constexpr int kSplitUnitRows = 2;     // rows per split work unit
 // Up to 256 consecutive splits of a concatenated activation.  Work units
 // [0, ceil(rows / 2)) are 2 consecutive rows of the launch, across split
 // boundaries.  With swizzled scales they are followed by one padding unit per
-// split whose last 128-row band has 1..31 live rows.
+// split whose last 128-row band has 1..31 live rows (dispatched first).
 struct SplitArgs {
     const uint16_t *src;  // global row 0 of this launch's first split
     uint8_t *payload;     // same row
