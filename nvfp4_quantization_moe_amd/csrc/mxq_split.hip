@@ -28,7 +28,11 @@
 //   4 consecutive rows (512 or 256 threads)                           33-34.6 / 29.4-31
 //   2 consecutive rows (256 threads)                                  33.3-34.4 / 29.1
 //   same, 4 consecutive units on one XCD                              32.1-32.3 / 29.3
-//   same, padding units dispatched first (here)                       30.8-31.2 / 28.7-28.9
+//   same, padding units dispatched first                              30.8-31.2 / 28.7-28.9
+//   same, 8, 16 or 64 units per XCD                                   30.0-30.8 / 28.8-30.1
+//   same, 32 units per XCD (here)                                     30.1-30.2 / 29.0-29.1
+//   (64 per XCD slows MXFP8 by 0.3-0.7 us.  Lanes on consecutive tiles of
+//   one row, 64 lines per wave store instead of 32, cost about 1 us.)
 //   1 row (128 threads)                                               38 / 32
 //
 // Splitting a band's padding over units of 16 or 4 tiles sped small
@@ -86,16 +90,16 @@ void k_split(const SplitArgs a) {
     int it = 0;  // row-scaled step counter, uniform over the workgroup
     for (int u0 = blockIdx.x; u0 < a.total_units; u0 += gridDim.x) {
         // swizzled: the padding units take the first dispatch slots, so their
-        // stores overlap the row units instead of trailing them; the 4 row
-        // units (8 rows) whose codes share 16-byte lines meet in one L2, which
-        // merges their partial-line stores
+        // stores overlap the row units instead of trailing them; 32 consecutive
+        // row units (64 rows, whose codes fill the 16-byte lines of half a
+        // band) meet in one L2, which merges their partial-line stores
         int u = u0;
         if (kSwz) {
             const int pads = a.total_units - n_row_units;
             u = u0 < pads ? n_row_units + u0 : u0 - pads;
         }
         if ((int)gridDim.x == a.total_units && u < n_row_units)
-            u = xcd_grouped_unit<4>(u, n_row_units);
+            u = xcd_grouped_unit<32>(u, n_row_units);
         if (kSwz && u >= n_row_units) {
             // padding unit of split s, whose last band has fewer than 32
             // live rows: the 16-byte chunks with no live row are zeroed
