@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Summarize three rocprofv3 runs of bench.py into profiles/*.md and
+profiles/hbm_traffic.json (the per-launch HBM traffic that bench.py reports).
+
+    python bench_profiles.py DIR
+
+DIR holds the runs' output folders: prof_kt (kernel trace), prof_fetch
+(FETCH_SIZE) and prof_write (WRITE_SIZE), made by the commands that each
+summary lists.  The counter runs add a 1 GiB device copy (bench.py
+--calib-copy); what the counters read for it calibrates them to bytes.
+Kernels are told apart by name, template arguments and grid size; where one
+grid serves several workloads, by dispatch order.
+"""
+import argparse
+import collections
+import csv
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+SOURCES = {
+    "grouped": ["mxq_grouped.hip", "mxq_device.h", "mxq_internal.h"],
+    "split": ["mxq_split.hip", "mxq_device.h", "mxq_internal.h"],
+    "fused": ["mxq_fused.hip", "mxq_device.h", "mxq_internal.h"],
+}
+FMT = {"0": "MXFP8", "1": "NVFP4"}
+LAY = {"0": "LINEAR", "1": "SWIZZLED"}
+GIB = 1 << 30
+
+CMD_KT = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+          "-d $OUT/prof_kt -o kt -- python3 $REPO/bench.py --steps 5 --warmup 1 --no-cpu-baseline")
+CMD_F = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+         "-d $OUT/prof_fetch -o f -- python3 $REPO/bench.py --steps 2 --warmup 1 "
+         "--no-cpu-baseline --calib-copy")
+CMD_W = CMD_F.replace("FETCH_SIZE", "WRITE_SIZE").replace("prof_fetch", "prof_write").replace(
+    "-o f ", "-o w ")
+HDR = ("Commands (`$REPO` is the repository root, `$OUT` an output folder; each counter in a run "
+       "of its own), summarized by `python bench_profiles.py $OUT`:\n\n```\n"
+       + CMD_KT + "\n" + CMD_F + "\n" + CMD_W + "\n```\n\n")
+
+
+def sf_bytes(rows, C, layout):
+    return rows * C if layout == 0 else -(-rows // 128) * 128 * (-(-C // 4) * 4)
+
+
+def avg(v):
+    return sum(v) / len(v) if v else float("nan")
+
+
+def read_counters(path):
+    """[(dispatch, kernel, grid threads, bytes)] and the calibration copy's bytes."""
+    rows, calib = [], None
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            n = r["Kernel_Name"]
+            v = float(r["Counter_Value"]) * 1024  # KiB -> bytes
+            if n.startswith("__amd_rocclr_copyBuffer") and calib is None and v > 1e8:
+                calib = v  # the first large copy: the 1 GiB calibration copy
+            rows.append((int(r["Dispatch_Id"]), n, int(r["Grid_Size"]), v))
+    if calib is None:
+        raise SystemExit(f"{path}: no calibration copy (run bench.py with --calib-copy)")
+    return rows, calib
+
+
+def read_trace(path):
+    """[(dispatch, kernel, grid threads, duration ns, start ns, end ns)] in dispatch order."""
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], g, e - s, s, e))
+    return sorted(rows)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("dir", help="folder holding prof_kt, prof_fetch and prof_write")
+    d = ap.parse_args().dir
+    sys.path.insert(0, ROOT)
+    import bench
+    from nvfp4_quantization_moe_amd import workloads
+
+    fetch, cf = read_counters(os.path.join(d, "prof_fetch", "f_counter_collection.csv"))
+    write, cw = read_counters(os.path.join(d, "prof_write", "w_counter_collection.csv"))
+    trace = read_trace(os.path.join(d, "prof_kt", "kt_kernel_trace.csv"))
+    f_scale, w_scale = GIB / cf, GIB / cw
+    calib = (f"Calibration: the 1 GiB device copy `--calib-copy` adds (`__amd_rocclr_copyBuffer`) "
+             f"reads {cf / 1024:,.1f} KiB of FETCH_SIZE and writes {cw / 1024:,.1f} KiB of "
+             f"WRITE_SIZE, so FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by "
+             f"{w_scale:.4f} to give bytes.\n")
+
+    def select(rows, match):
+        return [x for x in rows if match(x[1], x[2])]
+
+    def pmc(match, alg, pick=None):
+        fv, wv = select(fetch, match), select(write, match)
+        if pick:
+            fv, wv = pick(fv), pick(wv)
+        fb = avg([x[3] for x in fv]) * f_scale
+        wb = avg([x[3] for x in wv]) * w_scale
+        return len(fv), fb, wb, (fb + wb) / alg
+
+    def src(kind):
+        return {"sources": SOURCES[kind], "source_sha256": bench.source_hash(SOURCES[kind])}
+
+    out = {"fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+
+    def write_md(name, title, body):
+        with open(os.path.join(PROFILES, name), "w") as fh:
+            fh.write(f"# {title}\n\n" + HDR + body)
+
+    # ------------------------------------------------------------ grouped
+    shapes = workloads.QWEN3_235B_A22B
+    lines_t, lines_c = [], []
+    for f in "01":
+        for l in "01":
+            name = f"k_grouped<{FMT[f]},{LAY[l]}>"
+            per_alg, per_traf = [], []
+            for p, (r, c) in shapes.items():
+                fmt = int(f)
+                pw = c if fmt == 0 else c // 2
+                C = c // (32 if fmt == 0 else 16)
+                alg = 16 * (r * c * 2 + r * pw + sf_bytes(r, C, int(l)) + (4 if fmt else 0))
+                units = 16 * (-(-r // 128) * 128 // 16 if l == "1" else -(-r // 16)) * (-(-c // 512))
+                m = (lambda n, g, f=f, l=l, grid=units * 256:
+                     f"k_grouped<{f}, {l}, false>" in n and g == grid)
+                dur = [x[3] for x in select(trace, m)]
+                n, fb, wb, ratio = pmc(m, alg)
+                lines_t.append(f"| {name} | {p} | {len(dur)} | {avg(dur) / 1e3:,.2f} | "
+                               f"{min(dur) / 1e3:,.2f} | {max(dur) / 1e3:,.2f} | {alg / avg(dur):,.0f} |")
+                lines_c.append(f"| {name} | {p} | {n} | {alg:,} | {fb:,.0f} | {wb:,.0f} | {ratio:.4f} |")
+                per_alg.append(alg)
+                per_traf.append(fb + wb)
+            out["kernels"][name] = {
+                "workload": "Qwen3-235B-A22B-shaped layer, 16 experts per launch, mean of the "
+                            "gate_up and down launches", **src("grouped"),
+                "traffic_bytes_per_launch": round(avg(per_traf)),
+                "alg_bytes_per_launch": round(avg(per_alg)),
+                "ratio": round(avg(per_traf) / avg(per_alg), 4)}
+    write_md("k_grouped_qwen3_235b_layer.md",
+             "k_grouped -- Qwen3-235B-A22B-shaped MoE layer, 16 experts per launch, MI355X",
+             "## Kernel trace (per dispatch, from kt_kernel_trace.csv)\n\n"
+             "gate_up = 16 x bf16 [3072,4096], down = 16 x bf16 [4096,1536]; 6 dispatches each "
+             "(1 warm-up + 5 timed steps).  GB/s = algorithmic bytes / average duration.\n\n"
+             "| kernel | launch | n | avg us | min us | max us | GB/s |\n|---|---|---|---|---|---|---|\n"
+             + "\n".join(lines_t) + "\n\n"
+             "The benchmark's `per_kernel.avg_us` comes from HIP events at the boundaries of each "
+             "run of 8 same-kind launches (run time over 8, mean of gate_up and down), so it "
+             "includes the gaps between launches and reads a few us longer than the trace's "
+             "per-dispatch average.\n\n"
+             "## HBM traffic (FETCH_SIZE + WRITE_SIZE per dispatch)\n\n" + calib + "\n"
+             "| kernel | launch | n | algorithmic B | fetch B | write B | traffic / algorithmic |\n"
+             "|---|---|---|---|---|---|---|\n" + "\n".join(lines_c) + "\n")
+
+    # ------------------------------------- grouped against per-expert dispatch
+    # Qwen3-30B-A3B layer, MXFP8 swizzled: each timed call issues 8 gate_up + 8
+    # down grouped launches, or 128 + 128 single-expert launches, back to back
+    rows_l, spans = [], {}
+    for kind, per in (("grouped", 16), ("per-expert", 1)):
+        grids = {p: per * (-(-r // 128) * 128 // 16) * (-(-c // 512)) * 256
+                 for p, (r, c) in workloads.QWEN3_30B_A3B.items()}
+        seq = [x for x in trace if "k_grouped<0, 1, false>" in x[1] and x[2] in grids.values()]
+        n_call = 2 * 128 // per  # launches per layer
+        layers = [seq[i:i + n_call] for i in range(0, len(seq) - n_call + 1, n_call)]
+        kern = [sum(x[3] for x in L) for L in layers]
+        span = [L[-1][5] - L[0][4] for L in layers]
+        spans[kind] = (n_call, avg(kern), avg(span))
+        for p, g in grids.items():
+            dur = [x[3] for x in seq if x[2] == g]
+            rows_l.append(f"| {kind} | {p} | {g // 256} | {len(dur)} | {avg(dur) / 1e3:,.2f} |")
+    (ng, kg, sg), (ne, ke, se) = spans["grouped"], spans["per-expert"]
+    alg30 = sum(128 * (r * c * 3 + sf_bytes(r, c // 32, 1))
+                for r, c in workloads.QWEN3_30B_A3B.values())
+    write_md("k_grouped_qwen3_30b_a3b_grouped_vs_per_expert.md",
+             "k_grouped -- Qwen3-30B-A3B-shaped MoE layer, MXFP8 swizzled: 16 grouped launches "
+             "against 256 per-expert launches, MI355X",
+             "128 experts of gate_up bf16 [1536,2048] and 128 of down bf16 [2048,768] "
+             f"({alg30:,} algorithmic bytes per layer).  Grouped: 16 experts per launch, "
+             "8 + 8 launches; per-expert: one launch per expert, 128 + 128.  The same kernel "
+             "and bytes either way.\n\n"
+             "| dispatch | launch | workgroups | n | avg us |\n|---|---|---|---|---|\n"
+             + "\n".join(rows_l) + "\n\n"
+             "| per layer | launches | kernel time us (sum) | traced span us (first start to last end) | GB/s over the span |\n"
+             "|---|---|---|---|---|\n"
+             f"| grouped | {ng} | {kg / 1e3:,.1f} | {sg / 1e3:,.1f} | {alg30 / sg:,.0f} |\n"
+             f"| per-expert | {ne} | {ke / 1e3:,.1f} | {se / 1e3:,.1f} | {alg30 / se:,.0f} |\n\n"
+             f"Each launch beyond the 16 grouped ones costs {(ke - kg) / (ne - ng) / 1e3:.2f} us of "
+             "kernel time: the fixed ramp and tail of a launch, which grouping pays once per 16 "
+             "experts.  Kernel tracing adds its own host-side cost to every launch, so the traced "
+             f"span ({(se - sg) / (ne - ng) / 1e3:.2f} us per extra launch) overstates the gap; "
+             "bench.py reports the untraced layer times "
+             "(`other_workloads.qwen3_30b_a3b_layer_mxfp8_swizzled`).\n")
+
+    # ------------------------------------------------ encode scales from data
+    r, c = shapes["gate_up"]
+    gq = 16 * (-(-r // 128) * 128 // 16) * (c // 512) * 256
+    alg_q = 16 * (r * c * 2 + r * c // 2 + sf_bytes(r, c // 16, 1) + 8)
+    alg_a = 16 * r * c * 2
+    rows_a = []
+    for kname, m, alg in (
+            ("k_amax", lambda n, g: n.startswith("mxq::k_amax"), alg_a),
+            ("k_grouped<NVFP4,SWIZZLED,auto>",
+             lambda n, g: "k_grouped<1, 1, true>" in n and g == gq, alg_q)):
+        dur = [x[3] for x in select(trace, m)]
+        n, fb, wb, ratio = pmc(m, alg)
+        rows_a.append(f"| {kname} | {len(dur)} | {avg(dur) / 1e3:,.2f} | {alg:,} | "
+                      f"{alg / avg(dur):,.0f} | {fb:,.0f} | {wb:,.0f} | {ratio:.4f} |")
+    dz = [x[3] for x in select(trace, lambda n, g: n.startswith("mxq::k_zero_slots"))]
+    write_md("k_amax_auto_scale_qwen3_235b_gate_up.md",
+             "nvfp4_quant_grouped_auto -- 16 x bf16 [3072,4096] (Qwen3-235B-A22B gate_up), "
+             "swizzled, MI355X",
+             "Three kernels per call: k_zero_slots (16 accumulators), k_amax (reads the input), "
+             "k_grouped<NVFP4,SWIZZLED> with encode scales from the amax (reads it again).  "
+             f"k_zero_slots: {len(dz)} dispatches, {avg(dz) / 1e3:.2f} us average.\n\n" + calib + "\n"
+             "| kernel | n | avg us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
+             "|---|---|---|---|---|---|---|---|\n" + "\n".join(rows_a) + "\n")
+    out["kernels"]["k_amax"] = src("grouped")
+
+    # -------------------------------------------------------------- split
+    T, H = 8192, 7168
+    _, split = workloads.routed_activation()
+    rows_s = []
+    for key, (f, rs) in {"nvfp4": ("1", "false"), "nvfp4_row_scaled": ("1", "true"),
+                         "mxfp8": ("0", "false")}.items():
+        for l in "01":
+            fmt = int(f)
+            C = H // (32 if fmt == 0 else 16)
+            pay = T * (H if fmt == 0 else H // 2)
+            alg = (T * H * 2 + pay + sum(sf_bytes(m, C, int(l)) for m in split) + 4 * T
+                   + (4 if key == "nvfp4" else 0))
+            m = lambda n, g, f=f, rs=rs, l=l: f"k_split<{f}, {rs}, {l}, 7>" in n
+            dur = [x[3] for x in select(trace, m)]
+            n, fb, wb, ratio = pmc(m, alg)
+            rows_s.append(f"| {key} | {LAY[l]} | {len(dur)} | {avg(dur) / 1e3:,.2f} | {alg:,} | "
+                          f"{alg / avg(dur):,.0f} | {fb:,.0f} | {wb:,.0f} | {ratio:.4f} |")
+            out["kernels"][f"k_split<{key},{LAY[l]}>"] = {
+                "workload": "routed activation bf16 [8192,7168], 256 experts (10 empty)",
+                **src("split"), "traffic_bytes_per_launch": round(fb + wb),
+                "alg_bytes_per_launch": alg, "ratio": round(ratio, 4)}
+    write_md("k_split_routed_8192x7168.md",
+             "k_split -- routed activation bf16 [8192,7168] split over 256 experts "
+             "(10 empty, 19-55 rows each), MI355X",
+             "Algorithmic bytes: bf16 input + payload + every expert's (padded) scale region + "
+             "4 B of row amax per row.  8 input copies rotate (more than the 256 MB last-level "
+             "cache).\n\n" + calib + "\n"
+             "| form | scales | n | avg us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
+             "|---|---|---|---|---|---|---|---|---|\n" + "\n".join(rows_s) + "\n")
+
+    # -------------------------------------------------------------- fused
+    rows_f = []
+    for f in "01":
+        fmt = int(f)
+        by_grid = collections.defaultdict(list)
+        for Tt in (1, 16, 64, 256, 1024, 4096):
+            # swizzled units cover the padding rows: sixteen waves per row up to
+            # T = 512, four up to 1536, else two waves and four rows per unit
+            rt = -(-Tt // 128) * 128
+            grid = rt * 1024 if Tt <= 512 else rt * 256 if Tt <= 1536 else rt // 4 * 512
+            by_grid[grid].append(Tt)
+        for grid, Ts in by_grid.items():
+            for k, Tt in enumerate(Ts):
+                pw = H if fmt == 0 else H // 2
+                nsc = sf_bytes(Tt, H // (32 if fmt == 0 else 16), 1)
+                alg = Tt * H * 8 + Tt * pw + nsc + 2 * H + (4 if fmt else 0)
+                m = lambda n, g, f=f, grid=grid: f"k_fused<{f}, 1," in n and g == grid
+
+                def nth(rows, k=k, nT=len(Ts)):  # T values sharing a grid run in order
+                    per = len(rows) // nT
+                    return rows[k * per:(k + 1) * per]
+                dur = [x[3] for x in nth(select(trace, m))]
+                n, fb, wb, ratio = pmc(m, alg, nth)
+                rows_f.append(f"| {FMT[f]} | {Tt} | {len(dur)} | {avg(dur) / 1e3:,.2f} | {alg:,} | "
+                              f"{alg / avg(dur):,.0f} | {fb:,.0f} | {wb:,.0f} | {ratio:.4f} |")
+                if Tt == 4096:
+                    out["kernels"][f"k_fused<{FMT[f]},SWIZZLED>"] = {
+                        "workload": "residual + RMSNorm + quantize, T=4096, H=7168", **src("fused"),
+                        "traffic_bytes_per_launch": round(fb + wb), "alg_bytes_per_launch": alg,
+                        "ratio": round(ratio, 4)}
+    write_md("k_fused_rmsnorm_h7168.md",
+             "k_fused -- residual add + RMSNorm + quantize, H = 7168, swizzled scales, MI355X",
+             "Algorithmic bytes: x, residual in (4 B/elem), residual_out, norm_out (4 B/elem), "
+             "payload, padded scales, gamma.  T <= 512 runs sixteen waves per row (1024-thread "
+             "workgroups), T = 1024 four (256 threads), one row per workgroup (the padding rows "
+             "of a swizzled 128-row tile are workgroups of their own); T = 4096 runs two waves "
+             "per row, four rows per 512-thread workgroup.  T = 1, 16 and 64 share one grid "
+             "(128 workgroups), as do T = 256 and 1024; their dispatches are told apart by "
+             "order.\n\n" + calib + "\n"
+             "| format | T | n | avg us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
+             "|---|---|---|---|---|---|---|---|---|\n" + "\n".join(rows_f) + "\n")
+
+    # ------------------------------------------------------------ swizzle
+    rs_, cs_ = 16 * 3072, 128
+    alg = rs_ * cs_ + -(-rs_ // 128) * 128 * cs_
+    m = lambda n, g: n.startswith("mxq::k_swizzle")
+    dur = [x[3] for x in select(trace, m)]
+    n, fb, wb, ratio = pmc(m, alg)
+    write_md("k_swizzle_49152x128.md",
+             "k_swizzle -- linear MXFP8 scales of a 16-expert Qwen3-235B-A22B gate_up launch "
+             "(u8 [49152,128]) to the swizzled 128x4 layout, MI355X",
+             "Algorithmic bytes: the linear matrix in, the swizzled matrix out.  4 input/output "
+             "pairs rotate.\n\n" + calib + "\n"
+             "| kernel | n | avg us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
+             "|---|---|---|---|---|---|---|---|\n"
+             f"| k_swizzle | {len(dur)} | {avg(dur) / 1e3:,.2f} | {alg:,} | {alg / avg(dur):,.0f} | "
+             f"{fb:,.0f} | {wb:,.0f} | {ratio:.4f} |\n")
+    out["kernels"]["k_swizzle"] = {
+        "workload": "u8 [49152,128] linear -> swizzled", **src("fused"),
+        "traffic_bytes_per_launch": round(fb + wb), "alg_bytes_per_launch": alg,
+        "ratio": round(ratio, 4)}
+
+    with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    for name in sorted(os.listdir(PROFILES)):
+        if name.endswith(".md"):
+            print(f"wrote profiles/{name}")
+
+
+if __name__ == "__main__":
+    main()
