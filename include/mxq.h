@@ -221,9 +221,11 @@ int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual
  * scale_swizzle -- convert a linear [rows, sf_cols] scale matrix to the
  * swizzled 128x4 layout, zero padded [RL-3804, Summary: receiver-side layout
  * conversion; TRT-17453, invariance-test commit: the two layouts agree].
- *   linear    device u8 [rows, sf_cols]
+ *   linear    device u8 [rows, sf_cols], any alignment
  *   swizzled  device u8 [round_up(rows,128) * round_up(sf_cols,4)], 16-byte
  *             aligned
+ * 0 <= rows < 2^40 and 1 <= sf_cols < 2^31, else MXQ_EINVAL; rows == 0 is
+ * MXQ_OK with no launch.
  */
 int scale_swizzle(const void *linear, int64_t rows, int64_t sf_cols, void *swizzled,
                   void *stream);

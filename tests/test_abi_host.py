@@ -197,6 +197,8 @@ def test_swizzle_validation():
     assert L.scale_swizzle(0, 4, 4, A, None) == EINVAL
     assert L.scale_swizzle(A, 4, 4, A + 4, None) == ESHAPE
     assert L.scale_swizzle(0, 0, 4, 0, None) == OK
+    assert L.scale_swizzle(A, 1 << 40, 4, A, None) == EINVAL     # rows < 2^40
+    assert L.scale_swizzle(A, 4, 1 << 31, A, None) == EINVAL     # sf_cols < 2^31
 
 
 def test_binding_refuses_cpu_tensors():
