@@ -147,6 +147,41 @@ def test_empty_expert_with_zero_strides(orc):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+def test_linear_scales_at_odd_offsets(orc, fmt):
+    """Linear scale matrices may start at any byte.  Three experts' scales sit
+    at byte offsets 1, 2 and 3 (mod 16) of one canary-filled buffer, so the
+    rows that would leave as 16-byte stores leave byte by byte; the canary
+    between the regions stays."""
+    rng = torch.Generator().manual_seed(31 + fmt)
+    cols = 1024
+    xs_cpu = [(torch.randn(r, cols, generator=rng) * 3).to(torch.bfloat16) for r in (70, 33, 16)]
+    xs = [x.to(DEV) for x in xs_cpu]
+    gs = torch.cat([g_of(x) for x in xs]) if fmt == 1 else None
+    n_sc = [mxq.scale_bytes(x.shape[0], cols, fmt, mxq.LINEAR) for x in xs]
+    starts, pos = [], 0
+    for k, n in enumerate(n_sc):
+        pos = (pos + 15) // 16 * 16 + 16 + k + 1  # a canary gap, then offset k + 1
+        starts.append(pos)
+        pos += n
+    total = pos + 16
+    whole = torch.full((total,), CANARY, dtype=torch.uint8, device=DEV)
+    scs = [whole[st:st + n] for st, n in zip(starts, n_sc)]
+    pw = cols if fmt == 0 else cols // 2
+    pays = [torch.empty(x.shape[0], pw, dtype=torch.uint8, device=DEV) for x in xs]
+    say("odd linear scale offsets", fmt)
+    mxq.mx_quant_grouped(fmt, mxq.LINEAR, xs, pays, scs, gs)
+    torch.cuda.synchronize()
+    w = u8(whole)
+    outside = np.ones(total, bool)
+    for st, n in zip(starts, n_sc):
+        outside[st:st + n] = False
+    assert np.all(w[outside] == CANARY)
+    for i, x in enumerate(xs_cpu):
+        p, sc = oracle_entry(orc, fmt, orc.LINEAR, x, float(gs[i]) if fmt == 1 else 1.0)
+        assert np.array_equal(u8(pays[i]), p.ravel()) and np.array_equal(u8(scs[i]), sc), i
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_strided_source_rows(orc, fmt):
     say("strided src", fmt)
     big = (torch.randn(96, 1024) * 3).to(torch.bfloat16)

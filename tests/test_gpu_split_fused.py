@@ -165,6 +165,19 @@ def test_scale_swizzle(orc, R, C):
     assert np.array_equal(u8(out), orc.scale_swizzle(lin.numpy()))
 
 
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_scale_swizzle_unaligned_linear(orc, off):
+    """A linear matrix at a byte offset: 128 columns would take word loads,
+    the misaligned base must take the byte path."""
+    R, C = 300, 128
+    host = torch.randint(0, 256, (R * C + 4,), dtype=torch.int32).to(torch.uint8)
+    say("swizzle unaligned", off)
+    lin = host.to(DEV)[off:off + R * C].view(R, C)
+    got = mxq.scale_swizzle(lin)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(got), orc.scale_swizzle(host[off:off + R * C].view(R, C).numpy()))
+
+
 def test_swizzle_of_linear_equals_swizzled_quant(orc):
     x = (torch.randn(300, 4096) * 0.02).to(torch.bfloat16).to(DEV)
     say("layouts agree")

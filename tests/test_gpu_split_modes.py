@@ -161,15 +161,42 @@ def test_split_many_launches(orc):
             check(orc, fmt, x_cpu, split, layout)
 
 
+@pytest.mark.parametrize("mode", ["nvfp4", "mxfp8"])
+def test_split_linear_scales_at_odd_offset(orc, mode):
+    """Linear split scales may start at any byte: the bulk buffer at byte
+    offsets 1..3 (mod 16) takes byte stores for rows that would leave as
+    16-byte runs; the canary before and after stays."""
+    fmt = mxq.MXFP8 if mode == "mxfp8" else mxq.NVFP4
+    split = [0, 70, 33, 1, 0, 16]
+    T, H = sum(split), 1024
+    x_cpu = extreme_rows(T, H, seed=61)
+    x = x_cpu.to(DEV)
+    total = mxq.split_scale_offset(split, len(split), H, fmt, mxq.LINEAR)
+    g = torch.tensor([37.0], dtype=torch.float32, device=DEV)
+    op, os_, oa = orc.split(fmt, bf16_bits(x_cpu), split, g=37.0, layout=mxq.LINEAR)
+    for off in (1, 2, 3):
+        whole = torch.full((total + 32,), CANARY, dtype=torch.uint8, device=DEV)
+        sc = whole[off:off + total]
+        say("split odd linear scale offset", mode, off)
+        call = mxq.SplitCall(mode, x, split, mxq.LINEAR, g if mode == "nvfp4" else None,
+                             scales=sc)
+        p, s, a = call()
+        torch.cuda.synchronize()
+        w = u8(whole)
+        assert np.all(w[:off] == CANARY) and np.all(w[off + total:] == CANARY)
+        assert np.array_equal(u8(p), op.ravel()) and np.array_equal(u8(s), os_)
+        assert np.array_equal(a.cpu().numpy(), oa)
+
+
 LONG_SPLITS = ([0, 300, 129, 0, 500], [128, 256, 1], [1000], [128, 128])
 
 
 @pytest.mark.parametrize("mode", ["nvfp4", "nvfp4_row_scaled", "mxfp8"])
 @pytest.mark.parametrize("layout", [0, 1])
 def test_split_long_experts(orc, mode, layout):
-    """Experts of 128 rows or more on average take the 8-row units (the
-    short-expert sets above take whole tile lines): same bytes as the oracle,
-    also with capped grids."""
+    """Experts of 128 rows or more: whole 128-row bands, rows of one unit in
+    two experts, bands with no padding unit: same bytes as the oracle, also
+    with capped grids."""
     fmt = mxq.MXFP8 if mode == "mxfp8" else mxq.NVFP4
     for k, split in enumerate(LONG_SPLITS):
         T, H = sum(split), 1536
