@@ -126,6 +126,24 @@ def test_widest_rows(orc, fmt, layout):
             assert np.array_equal(scs[i], s), (cols, i)
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_narrowest_rows(orc, fmt, layout):
+    """Rows of one block and of three (one 512-column chunk, mostly idle
+    lanes; swizzled scale columns padded to a tile)."""
+    rng = torch.Generator().manual_seed(91 + 10 * fmt + layout)
+    block = 32 if fmt == 0 else 16
+    for cols in (block, 3 * block):
+        say("narrow rows", fmt, layout, cols)
+        xs_cpu = [(torch.randn(r, cols, generator=rng) * 5).to(torch.bfloat16) for r in (1, 130, 300)]
+        xs = [x.to(DEV) for x in xs_cpu]
+        gs = torch.cat([g_of(x) for x in xs]) if fmt == 1 else None
+        pays, scs = run_grouped(fmt, layout, xs, gs)
+        for i, x in enumerate(xs_cpu):
+            p, s = oracle_entry(orc, fmt, layout, x, float(gs[i]) if fmt == 1 else 1.0)
+            assert np.array_equal(pays[i], p.ravel()) and np.array_equal(scs[i], s), (cols, i)
+
+
 def test_empty_expert_with_zero_strides(orc):
     """A zero-row expert whose strides are (0, 0) (an empty array from numpy)
     is accepted among ordinary experts and changes none of their bytes."""

@@ -208,6 +208,19 @@ def _fused_check(orc, T, H, fmt, layout, seed, eps=1e-6, g=37.5):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+def test_fused_narrowest_rows(orc, fmt):
+    """The narrowest rows each layout accepts (linear: one or three blocks;
+    swizzled: one tile of four scale columns), where most of a row's waves
+    hold no column, with T on each side of the launcher's shape switches."""
+    block = 32 if fmt == 0 else 16
+    cases = [(mxq.LINEAR, block), (mxq.LINEAR, 3 * block), (mxq.SWIZZLED, 4 * block)]
+    for T in (1, 3, 300, 2000):
+        for layout, H in cases:
+            say("fused narrow, fmt", fmt, "layout", layout, "T", T, "H", H)
+            _fused_check(orc, T, H, fmt, layout, seed=T + H)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("layout", [0, 1])
 def test_fused_widths_both_row_splits(orc, fmt, layout):
     """Row widths with ragged 512-column tails, up to the 16384 maximum, on

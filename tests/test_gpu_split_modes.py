@@ -61,7 +61,7 @@ def extreme_rows(T, H, seed):
     bits[11] = 0x7F00                      # 2^127 everywhere: g clamps at 2^-100
     bits[11, ::7] = 0x7B80                 # ... with 2^120 entries
     bits[13, :] = 0x3F80
-    bits[13, 17] = 0x7F7F                  # bf16 max in one place
+    bits[13, min(17, H - 1)] = 0x7F7F      # bf16 max in one place
     return bits_to_bf16(bits)
 
 
@@ -159,6 +159,18 @@ def test_split_many_launches(orc):
         for layout in (0, 1):
             say("600 splits, fmt", fmt, "layout", layout)
             check(orc, fmt, x_cpu, split, layout)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_split_narrowest_rows(orc, fmt, layout):
+    """Rows of one block and of three: most lanes of both waves of a row hold
+    no column; swizzled scale columns are padded to a tile."""
+    split = [0, 1, 130, 31, 0, 2]
+    block = 32 if fmt == 0 else 16
+    for H in (block, 3 * block):
+        say("split narrow rows, fmt", fmt, "layout", layout, "H", H)
+        check(orc, fmt, extreme_rows(sum(split), H, seed=70 + H), split, layout)
 
 
 @pytest.mark.parametrize("mode", ["nvfp4", "mxfp8"])
