@@ -201,7 +201,10 @@ int mxfp8_quant_split(const void *src, int64_t total_rows, int64_t cols,
  *   x, residual  device bf16 [T, H]; gamma device bf16 [H]
  *   residual_out device bf16 [T, H] = bf16(x + residual)
  *   norm_out     device bf16 [T, H] = bf16(r * gamma / sqrt(mean(r^2) + eps)),
- *                fp32 arithmetic (within 1 bf16 ulp of the exact value)
+ *                fp32 arithmetic, within 1 bf16 ulp of the exact value while
+ *                every |r| < 2^64 / sqrt(H) and |r * gamma| < 2^127 (the fp32
+ *                sum of squares and products stay finite); beyond that the
+ *                value is unspecified
  *   payload, scales  fmt/layout quantization of norm_out (as mx_quant_grouped
  *                with rows = T, cols = H); swizzled scale rows T..round_up(T,128)
  *                are written as zero
@@ -209,7 +212,7 @@ int mxfp8_quant_split(const void *src, int64_t total_rows, int64_t cols,
  * H is a multiple of 32 (MXFP8) or 16 (NVFP4) and at most 16384; with the
  * swizzled layout H must also give a multiple of 4 scale columns (H % 128 == 0
  * for MXFP8, H % 64 == 0 for NVFP4), else MXQ_ESHAPE.  eps must be finite and
- * > 0; 0 <= T <= 2^31 - 128, else MXQ_EINVAL.  T == 0 is MXQ_OK with no
+ * at least 2^-126 (a normal fp32); 0 <= T <= 2^31 - 128, else MXQ_EINVAL.  T == 0 is MXQ_OK with no
  * launch.  All pointers 16-byte aligned.
  */
 int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual,

@@ -271,8 +271,10 @@ int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual
                         const float *global_scale, void *residual_out, void *norm_out,
                         void *payload, void *scales, void *stream) {
     if (!valid_fmt(fmt) || !valid_layout(layout)) return MXQ_EINVAL;
-    // rows padded to 128 must still index as int32
-    if (!(eps > 0.0f) || !(eps < 3.4e38f) || T < 0 || T > ((int64_t)1 << 31) - 128)
+    // eps a normal fp32 (a subnormal eps would let the fp32 sum of squares of
+    // a row of tiny values lose accuracy); rows padded to 128 must still index
+    // as int32
+    if (!(eps >= 0x1p-126f) || !(eps < 3.4e38f) || T < 0 || T > ((int64_t)1 << 31) - 128)
         return MXQ_EINVAL;
     if (H <= 0 || H % block_of(fmt) != 0 || H > kMaxFusedH) return MXQ_ESHAPE;
     const int64_t C = H / block_of(fmt);

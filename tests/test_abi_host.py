@@ -177,6 +177,8 @@ def test_fused_validation():
     assert _fused(eps=-1.0) == EINVAL
     assert _fused(eps=float("nan")) == EINVAL
     assert _fused(eps=float("inf")) == EINVAL
+    assert _fused(eps=2.0 ** -127) == EINVAL        # subnormal eps
+    assert _fused(eps=2.0 ** -126, T=0) == OK       # the smallest normal is accepted
     assert _fused(T=-1) == EINVAL
     assert _fused(T=(1 << 31) - 127) == EINVAL      # padded rows must index as int32
     assert _fused(fmt=3) == EINVAL

@@ -188,8 +188,8 @@ def test_swizzle_of_linear_equals_swizzled_quant(orc):
     assert torch.equal(conv, s_swz[0])
 
 
-def _fused_check(orc, T, H, fmt, layout, seed, eps=1e-6, g=37.5):
-    x_c, r_c, g_c = workloads.epilogue_inputs(T, H, seed=seed)
+def _fused_check(orc, T, H, fmt, layout, seed, eps=1e-6, g=37.5, inputs=None):
+    x_c, r_c, g_c = workloads.epilogue_inputs(T, H, seed=seed) if inputs is None else inputs
     x, r, gm = x_c.to(DEV), r_c.to(DEV), g_c.to(DEV)
     gs = torch.tensor([g], dtype=torch.float32, device=DEV)
     pw = H if fmt == mxq.MXFP8 else H // 2
@@ -205,6 +205,25 @@ def _fused_check(orc, T, H, fmt, layout, seed, eps=1e-6, g=37.5):
     assert bf16_ulp_diff(bf16_bits(no), ono).max() <= 1
     qp, qs = orc.quantize(fmt, layout, bf16_bits(no), g=g)
     assert np.array_equal(u8(pay), qp.ravel()) and np.array_equal(u8(sc), qs)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 2.0 ** -126])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_fused_row_magnitudes(orc, fmt, eps):
+    """Rows far from unit scale, inside the range the header states: x and
+    residual scaled by 2^53 (|r| up to about 2^56, squares summing to about
+    2^120 at H = 7168) down to 2^-80 (squares subnormal or lost, where eps
+    decides), with the smallest accepted eps too.  norm_out within 1 ulp,
+    the quantized form exact."""
+    T, H = 10, 7168
+    x_c, r_c, g_c = workloads.epilogue_inputs(T, H, seed=6)
+    k = torch.tensor([53.0, 40.0, 0.0, -20.0, -60.0, -63.0, -66.0, -70.0, -80.0, -10.0])
+    scale = torch.pow(2.0, k).reshape(T, 1)
+    xs = (x_c.float() * scale).to(torch.bfloat16)
+    rs = (r_c.float() * scale).to(torch.bfloat16)
+    for layout in (mxq.LINEAR, mxq.SWIZZLED):
+        say("fused magnitudes, fmt", fmt, "eps", eps, "layout", layout)
+        _fused_check(orc, T, H, fmt, layout, seed=0, eps=eps, inputs=(xs, rs, g_c))
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
