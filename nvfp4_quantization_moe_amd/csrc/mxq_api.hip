@@ -199,10 +199,13 @@ int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, i
         split_rows = whole;
         n_splits = 1;
     }
+    // Empty splits own no rows and no scale bytes, so the launches' tables
+    // list only the others: the prefix sums of rows, bands and padding units
+    // are the same, and a row's expert is then found in a few steps even when
+    // most experts are empty (decode-sized activations).
     int64_t row_base = 0, scale_base = 0;
-    for (int first = 0; first < n_splits; first += kMaxSplitsPerLaunch) {
-        const int n = n_splits - first < kMaxSplitsPerLaunch ? n_splits - first
-                                                             : kMaxSplitsPerLaunch;
+    int next = 0;  // the next split to place
+    while (next < n_splits) {
         SplitArgs a;
         memset(&a, 0, sizeof(a));
         a.src = static_cast<const uint16_t *>(src) + row_base * cols;
@@ -213,18 +216,22 @@ int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, i
         a.cols = (int32_t)cols;
         a.sf_cols = (int32_t)C;
         a.sf_stride = (int32_t)Cs;
-        a.n = n;
+        int n = 0;
         int64_t rows = 0, pads = 0, sbytes = 0, bands = 0;
-        for (int j = 0; j < n; ++j) {
-            const int64_t m = split_rows[first + j];
-            a.row_off[j] = (int32_t)rows;
-            a.unit_off[j] = (int32_t)pads;
-            a.band_off[j] = (int32_t)bands;
+        for (; next < n_splits && n < kMaxSplitsPerLaunch; ++next) {
+            const int64_t m = split_rows[next];
+            if (m == 0) continue;
+            a.row_off[n] = (int32_t)rows;
+            a.unit_off[n] = (int32_t)pads;
+            a.band_off[n] = (int32_t)bands;
+            ++n;
             rows += m;
             bands += (m + 127) / 128;
             pads += layout == MXQ_SF_SWIZZLED && m % 128 != 0 && m % 128 < 32 ? 1 : 0;
             sbytes += sf_bytes(m, C, layout);
         }
+        if (n == 0) break;  // only empty splits were left
+        a.n = n;
         a.row_off[n] = (int32_t)rows;
         a.unit_off[n] = (int32_t)pads;
         a.band_off[n] = (int32_t)bands;

@@ -67,7 +67,8 @@ struct GroupArgs {
 constexpr int kMaxSplitsPerLaunch = 256;
 constexpr int kSplitUnitRows = 2;     // rows per split work unit
 
-// Up to 256 consecutive splits of a concatenated activation.  Work units
+// Up to 256 consecutive non-empty splits of a concatenated activation (the
+// host leaves empty splits out: they own no rows and no scale bytes).  Work units
 // [0, ceil(rows / 2)) are 2 consecutive rows of the launch, across split
 // boundaries.  With swizzled scales they are followed by one padding unit per
 // split whose last 128-row band has 1..31 live rows (dispatched first).
