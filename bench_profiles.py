@@ -2,14 +2,15 @@
 """Summarize three rocprofv3 runs of bench.py into profiles/*.md and
 profiles/hbm_traffic.json (the per-launch HBM traffic that bench.py reports).
 
-    python bench_profiles.py DIR
+    python bench_profiles.py DIR [--out OUT]
 
 DIR holds the runs' output folders: prof_kt (kernel trace), prof_fetch
 (FETCH_SIZE) and prof_write (WRITE_SIZE), made by the commands that each
 summary lists.  The counter runs add a 1 GiB device copy (bench.py
 --calib-copy); what the counters read for it calibrates them to bytes.
 Kernels are told apart by name, template arguments and grid size; where one
-grid serves several workloads, by dispatch order.
+grid serves several workloads, by dispatch order.  A kernel the runs do not
+contain gets a row of n = 0 and NaN figures.  OUT defaults to profiles/.
 """
 import argparse
 import collections
@@ -75,10 +76,27 @@ def read_trace(path):
     return sorted(rows)
 
 
-def main():
+def rnd(x, nd=None):
+    """round(), or None for a kernel the runs did not contain (NaN)."""
+    if x != x:
+        return None
+    return round(x) if nd is None else round(x, nd)
+
+
+def lo(v):
+    return min(v) if v else float("nan")
+
+
+def hi(v):
+    return max(v) if v else float("nan")
+
+
+def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("dir", help="folder holding prof_kt, prof_fetch and prof_write")
-    d = ap.parse_args().dir
+    ap.add_argument("--out", default=PROFILES, help="where the summaries go")
+    args = ap.parse_args(argv)
+    d, out_dir = args.dir, args.out
     sys.path.insert(0, ROOT)
     import bench
     from nvfp4_quantization_moe_amd import workloads
@@ -109,7 +127,7 @@ def main():
     out = {"fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
 
     def write_md(name, title, body):
-        with open(os.path.join(PROFILES, name), "w") as fh:
+        with open(os.path.join(out_dir, name), "w") as fh:
             fh.write(f"# {title}\n\n" + HDR + body)
 
     # ------------------------------------------------------------ grouped
@@ -130,16 +148,16 @@ def main():
                 dur = [x[3] for x in select(trace, m)]
                 n, fb, wb, ratio = pmc(m, alg)
                 lines_t.append(f"| {name} | {p} | {len(dur)} | {avg(dur) / 1e3:,.2f} | "
-                               f"{min(dur) / 1e3:,.2f} | {max(dur) / 1e3:,.2f} | {alg / avg(dur):,.0f} |")
+                               f"{lo(dur) / 1e3:,.2f} | {hi(dur) / 1e3:,.2f} | {alg / avg(dur):,.0f} |")
                 lines_c.append(f"| {name} | {p} | {n} | {alg:,} | {fb:,.0f} | {wb:,.0f} | {ratio:.4f} |")
                 per_alg.append(alg)
                 per_traf.append(fb + wb)
             out["kernels"][name] = {
                 "workload": "Qwen3-235B-A22B-shaped layer, 16 experts per launch, mean of the "
                             "gate_up and down launches", **src("grouped"),
-                "traffic_bytes_per_launch": round(avg(per_traf)),
+                "traffic_bytes_per_launch": rnd(avg(per_traf)),
                 "alg_bytes_per_launch": round(avg(per_alg)),
-                "ratio": round(avg(per_traf) / avg(per_alg), 4)}
+                "ratio": rnd(avg(per_traf) / avg(per_alg), 4)}
     write_md("k_grouped_qwen3_235b_layer.md",
              "k_grouped -- Qwen3-235B-A22B-shaped MoE layer, 16 experts per launch, MI355X",
              "## Kernel trace (per dispatch, from kt_kernel_trace.csv)\n\n"
@@ -238,8 +256,8 @@ def main():
                           f"{alg / avg(dur):,.0f} | {fb:,.0f} | {wb:,.0f} | {ratio:.4f} |")
             out["kernels"][f"k_split<{key},{LAY[l]}>"] = {
                 "workload": "routed activation bf16 [8192,7168], 256 experts (10 empty)",
-                **src("split"), "traffic_bytes_per_launch": round(fb + wb),
-                "alg_bytes_per_launch": alg, "ratio": round(ratio, 4)}
+                **src("split"), "traffic_bytes_per_launch": rnd(fb + wb),
+                "alg_bytes_per_launch": alg, "ratio": rnd(ratio, 4)}
     write_md("k_split_routed_8192x7168.md",
              "k_split -- routed activation bf16 [8192,7168] split over 256 experts "
              "(10 empty, 19-55 rows each), MI355X",
@@ -277,8 +295,8 @@ def main():
                 if Tt == 4096:
                     out["kernels"][f"k_fused<{FMT[f]},SWIZZLED>"] = {
                         "workload": "residual + RMSNorm + quantize, T=4096, H=7168", **src("fused"),
-                        "traffic_bytes_per_launch": round(fb + wb), "alg_bytes_per_launch": alg,
-                        "ratio": round(ratio, 4)}
+                        "traffic_bytes_per_launch": rnd(fb + wb), "alg_bytes_per_launch": alg,
+                        "ratio": rnd(ratio, 4)}
     write_md("k_fused_rmsnorm_h7168.md",
              "k_fused -- residual add + RMSNorm + quantize, H = 7168, swizzled scales, MI355X",
              "Algorithmic bytes: x, residual in (4 B/elem), residual_out, norm_out (4 B/elem), "
@@ -308,14 +326,14 @@ def main():
              f"{fb:,.0f} | {wb:,.0f} | {ratio:.4f} |\n")
     out["kernels"]["k_swizzle"] = {
         "workload": "u8 [49152,128] linear -> swizzled", **src("fused"),
-        "traffic_bytes_per_launch": round(fb + wb), "alg_bytes_per_launch": alg,
-        "ratio": round(ratio, 4)}
+        "traffic_bytes_per_launch": rnd(fb + wb), "alg_bytes_per_launch": alg,
+        "ratio": rnd(ratio, 4)}
 
-    with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as fh:
+    with open(os.path.join(out_dir, "hbm_traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
-    for name in sorted(os.listdir(PROFILES)):
+    for name in sorted(os.listdir(out_dir)):
         if name.endswith(".md"):
-            print(f"wrote profiles/{name}")
+            print(f"wrote {os.path.join(out_dir, name)}")
 
 
 if __name__ == "__main__":
