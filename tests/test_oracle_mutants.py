@@ -18,6 +18,10 @@ MUTANTS = [
     ("exponent_rule_floor", "if (amax <= 448.0 * ldexp(1.0, c - 127))",
      "if (amax < 256.0 * ldexp(1.0, c - 126))"),
     ("no_ftz_on_reciprocal", "    if (scale < FLT_MIN)\n        return 0.0;\n", ""),
+    ("zero_block_scale_one", "    for (c = 0; c <= 254; ++c)\n        if (amax <= 448.0",
+     "    if (amax == 0.0)\n        return 127;\n    for (c = 0; c <= 254; ++c)\n        if (amax <= 448.0"),
+    ("scale_code_search_from_one", "    for (c = 0; c <= 254; ++c)\n        if (amax <= 448.0",
+     "    for (c = 1; c <= 254; ++c)\n        if (amax <= 448.0"),
     ("ties_away_from_zero", "return nearbyint(a / spacing) * spacing;",
      "return round(a / spacing) * spacing;"),
     ("nibbles_swapped", "payload[i / 2] |= (uint8_t)(q << (4 * (i & 1)));",
