@@ -45,6 +45,8 @@ MUTANTS = [
      "den = sqrt(ss / (double)(H - 1) + (double)eps);"),
     ("rmsnorm_eps_outside_root", "den = sqrt(ss / (double)H + (double)eps);",
      "den = sqrt(ss / (double)H) + (double)eps;"),
+    ("empty_split_padded_to_128", "    return round_up(rows, 128) * round_up(sf_cols, 4);",
+     "    return round_up(rows > 0 ? rows : 1, 128) * round_up(sf_cols, 4);"),
     ("split_offset_off_by_one", "for (j = 0; j < i && j < n; ++j)",
      "for (j = 0; j <= i && j < n; ++j)"),
     ("mx_element_scale_sign", "payload[i] = orc_e4m3_encode(orc_bf16_value(x[i]) * m);",
