@@ -222,8 +222,11 @@ void orc_mxfp8_block(const uint16_t *x, int n, uint8_t *payload, uint8_t *scale)
 /* shared by the fused gate/up.                                             */
 /* Reading fixed here: s = fp32(fp32(amax / 6) * g); the block scale code is  */
 /* E4M3(s); the element multiplier is fp32(g / decode(code)), zero when the  */
-/* decoded scale is zero or the multiplier is not a normal fp32 number; each */
-/* element is E2M1(fp32(x * m)); element 2j goes to the low nibble of byte j. */
+/* decoded scale is zero or the multiplier is not a normal fp32 number       */
+/* (subnormal, or infinite after overflow: the flush-to-zero of the block-   */
+/* scale reciprocal, [TRT-17453, Triton func commit], applied to any result  */
+/* outside the normal range); each element is E2M1(fp32(x * m)); element 2j  */
+/* goes to the low nibble of byte j.  g is any positive finite fp32 number.  */
 /* ----------------------------------------------------------------------- */
 
 void orc_nvfp4_block(const uint16_t *x, int n, float g, uint8_t *payload, uint8_t *scale)
@@ -243,11 +246,12 @@ void orc_nvfp4_block(const uint16_t *x, int n, float g, uint8_t *payload, uint8_
     s = t * g;       /* fp32 product, correctly rounded */
     k = orc_e4m3_encode((double)s);
     sq = (float)orc_e4m3_value(k);
+    assert(g > 0.0f && g <= FLT_MAX);
     m = 0.0f;
     if (sq != 0.0f) {
-        m = g / sq; /* fp32 division, correctly rounded */
-        if (!(m >= FLT_MIN))
-            m = 0.0f;
+        m = g / sq; /* fp32 division, correctly rounded (may overflow to inf) */
+        if (!(m >= FLT_MIN && m <= FLT_MAX))
+            m = 0.0f; /* not a normal number: flushed */
     }
     for (i = 0; i < n; i += 2)
         payload[i / 2] = 0;
@@ -307,6 +311,8 @@ int orc_quantize(int fmt, int layout, const uint16_t *src, int64_t rows, int64_t
         return -1;
     if (rows < 0 || cols <= 0 || cols % bs != 0 || ld < cols)
         return -1;
+    if (fmt == ORC_NVFP4 && !(g > 0.0f && g <= FLT_MAX))
+        return -1; /* the encode scale is a positive finite number */
     memset(scales, 0, (size_t)orc_sf_bytes(rows, C, layout)); /* padding is zero */
     for (r = 0; r < rows; ++r) {
         for (c = 0; c < C; ++c) {
@@ -345,21 +351,24 @@ int64_t orc_split_scale_offset(const int64_t *split_rows, int n, int i, int64_t 
  * pages print no formula; the convention that maps the amax onto the largest
  * E4M3 block scale (448) times the largest E2M1 element (6) gives
  * g = fp32(2688 / a), a correctly rounded fp32 division.  An all-zero input
- * takes g = 1 (any value quantizes it to zeros), and g is clamped to
- * [2^-100, 2^100], the range in which every block multiplier g / s_q stays a
- * finite normal fp32 number; only a < 2688 * 2^-100 or a > 2688 * 2^100
- * reach the clamp. */
+ * takes g = 1 (any value quantizes it to zeros).
+ *
+ * Range.  Every block multiplier is g / s_q with s_q an E4M3 value in
+ * [2^-9, 448].  From above, g is capped at FLT_MAX * 2^-9, the largest g for
+ * which g / 2^-9 is finite; only a < 2688 * 2^9 / FLT_MAX (about 2^-107.6)
+ * reaches the cap, and for a < 2688 / FLT_MAX the quotient itself overflows.
+ * No lower bound is needed: a <= FLT_MAX gives g >= 2688 / FLT_MAX (about
+ * 2^-116.6), so g / 448 stays above the smallest normal fp32 number. */
 float orc_nvfp4_encode_scale(float amax)
 {
-    float g, lo = (float)ldexp(1.0, -100), hi = (float)ldexp(1.0, 100);
+    const float g_max = FLT_MAX / 512.0f; /* exact: FLT_MAX * 2^-9 */
+    float g;
     assert(amax >= 0.0f && isfinite(amax));
     if (amax == 0.0f)
         return 1.0f;
     g = 2688.0f / amax; /* fp32 division, correctly rounded (may overflow to inf) */
-    if (g < lo)
-        g = lo;
-    if (g > hi)
-        g = hi;
+    if (g > g_max)
+        g = g_max;
     return g;
 }
 
@@ -409,6 +418,8 @@ int orc_split(int fmt, int row_scaled, const uint16_t *src, int64_t total_rows, 
     }
     if (sum != total_rows || cols <= 0 || cols % bs != 0)
         return -1;
+    if (fmt == ORC_NVFP4 && !row_scaled && !(g > 0.0f && g <= FLT_MAX))
+        return -1; /* the encode scale is a positive finite number */
     C = orc_sf_cols(cols, fmt);
     for (i = 0; i < n; ++i) {
         int64_t m = split_rows[i];

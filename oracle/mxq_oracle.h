@@ -84,7 +84,8 @@ int orc_split(int fmt, int row_scaled, const uint16_t *src, int64_t total_rows, 
               const int64_t *split_rows, int n, float g, int layout, uint8_t *payload,
               uint8_t *scales, float *row_amax);
 /* NVFP4 encode scale from an amax (a tensor's or a row's): 1 for amax 0,
- * else fp32(2688 / amax) clamped to [2^-100, 2^100]. */
+ * else fp32(2688 / amax), capped at FLT_MAX * 2^-9 (every block multiplier
+ * g / s_q then stays finite). */
 float orc_nvfp4_encode_scale(float amax);
 /* max |x| over a bf16 [rows, cols] tensor with row stride ld. */
 float orc_tensor_amax(const uint16_t *src, int64_t rows, int64_t cols, int64_t ld);

@@ -42,7 +42,8 @@ def hand_blocks():
             if not line or line.startswith("#"):
                 continue
             parts = line.split()
-            d = {"id": parts[0], "fmt": parts[1], "g": float(parts[2]), "scale": int(parts[3], 16)}
+            g = float.fromhex(parts[2]) if parts[2].startswith("0x") else float(parts[2])
+            d = {"id": parts[0], "fmt": parts[1], "g": g, "scale": int(parts[3], 16)}
             for p in parts[4:]:
                 k, v = p.split("=")
                 d[k] = _expand(v)

@@ -30,7 +30,7 @@ MUTANTS = [
      "(r % 32) * 4 + ((r % 128) / 32) * 16"),
     ("swizzle_tiles_column_major", "((r / 128) * tiles_per_row_band + c / 4) * 512",
      "((c / 4) * ((r / 128) + 1) + r / 128) * 512"),
-    ("nvfp4_multiplier_reciprocal", "m = g / sq; /* fp32 division, correctly rounded */",
+    ("nvfp4_multiplier_reciprocal", "m = g / sq; /* fp32 division, correctly rounded (may overflow to inf) */",
      "m = 1.0f / (sq / g);"),
     ("nvfp4_scale_divisor", "t = a / 6.0f;", "t = a / 4.0f;"),
     ("sign_of_zero_dropped", "uint8_t sign = signbit(v) ? 0x80 : 0x00;",
@@ -54,9 +54,17 @@ MUTANTS = [
     ("residual_not_rounded",
      "uint16_t rb = orc_bf16_round(orc_bf16_value(x[t * H + j]) + orc_bf16_value(res[t * H + j]));",
      "uint16_t rb = orc_bf16_round(orc_bf16_value(x[t * H + j]));"),
-    ("row_scale_unclamped", "    if (g > hi)\n        g = hi;\n", ""),
-    ("row_scale_clamped_at_flt_max", "    if (g > hi)\n        g = hi;\n",
+    ("row_scale_uncapped", "    if (g > g_max)\n        g = g_max;\n", ""),
+    ("row_scale_capped_at_flt_max", "    if (g > g_max)\n        g = g_max;\n",
      "    if (g > FLT_MAX)\n        g = FLT_MAX;\n"),
+    ("row_scale_capped_at_2_100", "const float g_max = FLT_MAX / 512.0f;",
+     "const float g_max = 0x1p100f;"),
+    ("row_scale_lower_clamp_2_m100", "    if (g > g_max)\n        g = g_max;\n",
+     "    if (g > g_max)\n        g = g_max;\n    if (g < 0x1p-100f)\n        g = 0x1p-100f;\n"),
+    ("nvfp4_overflowing_multiplier_kept", "if (!(m >= FLT_MIN && m <= FLT_MAX))",
+     "if (!(m >= FLT_MIN))"),
+    ("nvfp4_subnormal_multiplier_kept", "if (!(m >= FLT_MIN && m <= FLT_MAX))",
+     "if (!(m <= FLT_MAX))"),
     ("row_scale_zero_row_unity_dropped", "    if (amax == 0.0f)\n        return 1.0f;\n", ""),
     ("row_scale_without_e2m1_max", "g = 2688.0f / amax;", "g = 448.0f / amax;"),
     ("row_scaled_local_row_ignored",

@@ -39,15 +39,28 @@ def test_row_encode_scale_special_values(orc):
     assert orc.nvfp4_encode_scale(2688.0) == 1.0
     assert orc.nvfp4_encode_scale(1.0) == 2688.0
     assert orc.nvfp4_encode_scale(7.0) == 384.0
-    # clamp edges: 2688 * 2^-100 and 2688 * 2^100 are the largest / smallest
-    # amax values that do not clamp
-    lo = 2688.0 * 2.0 ** -100
-    hi = 2688.0 * 2.0 ** 100
-    assert orc.nvfp4_encode_scale(lo) == 2.0 ** 100
-    assert orc.nvfp4_encode_scale(lo / 2) == 2.0 ** 100
-    assert orc.nvfp4_encode_scale(hi) == 2.0 ** -100
-    assert orc.nvfp4_encode_scale(hi * 2) == 2.0 ** -100
     assert orc.nvfp4_encode_scale(3.0 * 2.0 ** 50) == np.float32(896.0 * 2.0 ** -50)
+    # The cap: G = FLT_MAX * 2^-9, the largest g with G / 2^-9 finite.  Below
+    # the smallest amax whose quotient 2688 / a (IEEE fp32 division, numpy)
+    # stays <= G, every amax gets G, including those whose quotient overflows.
+    f32 = np.float32
+    fmax = np.finfo(np.float32).max
+    G = f32(fmax) / f32(512)
+    assert float(G) == float.fromhex("0x1.fffffep+118")
+    assert np.isfinite(G / f32(2.0 ** -9))
+    a = f32(2688.0 * 512.0 / float(fmax))
+    while f32(2688.0) / a <= G:  # walk down to the first capped amax
+        a = np.nextafter(a, f32(0))
+    for v in (a, a / f32(3), f32(2.0 ** -120), f32(2.0 ** -133), f32(1e-45)):
+        assert orc.nvfp4_encode_scale(float(v)) == G, v
+    b = np.nextafter(a, f32(1))
+    assert orc.nvfp4_encode_scale(float(b)) == f32(2688.0) / b < G
+    # no lower bound: the largest bf16 and fp32 amax keep the plain quotient,
+    # and the multiplier under it for the largest block scale is still normal
+    for v in (f32(255.0 * 2.0 ** 120), f32(fmax)):
+        g = orc.nvfp4_encode_scale(float(v))
+        assert g == f32(2688.0) / v
+        assert f32(g) / f32(448.0) >= np.finfo(np.float32).tiny
 
 
 def _rows(T, H, seed, scale_spread=1.0):
