@@ -129,6 +129,17 @@ class HipTimingEvents:
         self.events = []
 
 
+def caller_encode_scales(amax):
+    """The caller's NVFP4 encode scales for the precomputed-scale calls: the
+    usual choice fp32(2688 / amax) (1 for an all-zero tensor), capped at
+    FLT_MAX * 2^-9 as the library caps the scales it derives itself.  Input
+    preparation, computed untimed; any positive finite fp32 is a valid g."""
+    import torch
+    a = amax.to(torch.float32)
+    g = torch.where(a > 0, torch.full_like(a, 2688.0) / a, torch.ones_like(a))
+    return torch.clamp(g, max=float.fromhex("0x1.fffffep+118"))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -169,7 +180,7 @@ def main():
         f"{shapes['down']} bf16")
     buf = {p: workloads.expert_stack(E, r, c, std=0.015, seed=5000 + k, device=dev)
            for k, (p, (r, c)) in enumerate(shapes.items())}
-    gsc = {p: workloads.encode_scale_from_amax(buf[p].float().abs().amax(dim=(1, 2))).contiguous()
+    gsc = {p: caller_encode_scales(buf[p].float().abs().amax(dim=(1, 2))).contiguous()
            for p in buf}
     torch.cuda.synchronize()
 
@@ -433,7 +444,7 @@ def extra_workloads(torch, mxq, workloads, dev):
     r, c = workloads.QWEN3_235B_A22B["gate_up"]
     stack = workloads.expert_stack(G, r, c, std=0.015, seed=5000, device=dev)
     auto = mxq.GroupedAutoCall(1, [stack[i] for i in range(G)])
-    gs = workloads.encode_scale_from_amax(stack.float().abs().amax(dim=(1, 2))).contiguous()
+    gs = caller_encode_scales(stack.float().abs().amax(dim=(1, 2))).contiguous()
     plain = mxq.GroupedCall(1, 1, [stack[i] for i in range(G)], auto.payloads, auto.scales, gs)
 
     def torch_amax_then_grouped(i):
@@ -456,7 +467,7 @@ def extra_workloads(torch, mxq, workloads, dev):
     # encode scale, row-scaled NVFP4, MXFP8; linear and swizzled scales
     x, split = workloads.routed_activation()
     xs = [x.to(dev) for _ in range(8)]
-    g = workloads.encode_scale_from_amax(xs[0].float().abs().amax()).reshape(1)
+    g = caller_encode_scales(xs[0].float().abs().amax()).reshape(1)
     T, H = x.shape
     am = torch.empty(T, dtype=torch.float32, device=dev)
     splits = {}

@@ -26,10 +26,13 @@
  * under an fp32 encode scale g (block scale s = fp32(fp32(amax/6) * g)
  * rounded to E4M3 with saturation; element multiplier fp32(g / s_q)), E2M1
  * elements saturating at 6, two per byte, element 2j in the low nibble of
- * byte j.  Every NVFP4 encode scale g must lie in [2^-100, 2^100] (a device
- * value the library cannot check; outside it results are unspecified).
- * Results are bit-identical to the definitions above, whatever the grouping,
- * split or launch shape.
+ * byte j; the multiplier is flushed to 0 when it is not a normal fp32 number
+ * (subnormal, or infinite after overflow), the NVFP4 form of the flush on the
+ * block-scale reciprocal.  An NVFP4 encode scale g may be any positive finite
+ * fp32 number, subnormal included (it is a device value the library cannot
+ * check: zero, negative, infinite or NaN g give unspecified bytes).  Results
+ * are bit-identical to the definitions above, whatever the grouping, split or
+ * launch shape.
  *
  * Scale layouts [TRT-17452, layout commit; TRT-17453, AllReduce epilogue
  * commit].  LINEAR: byte (r, c) of an [R, C] scale matrix at r*C + c.
@@ -48,9 +51,13 @@
  * allocates, copies or synchronizes, so every call may be captured in a HIP
  * graph.  Outputs must not alias inputs or each other.
  *
- * Errors.  Every call validates all arguments on the host first; on any error
- * it returns a nonzero mxq_status, launches nothing and writes nothing.
- * MXQ_ELAUNCH reports a failed kernel launch.
+ * Errors.  Every call validates all arguments on the host first; when a check
+ * fails it returns a nonzero mxq_status, launches nothing and writes nothing.
+ * MXQ_ELAUNCH reports a kernel launch that the HIP runtime rejected after
+ * validation passed.  A call that issues several launches
+ * (nvfp4_quant_grouped_auto; a split with more than 256 non-empty experts)
+ * may then have enqueued the launches before the failed one, so after
+ * MXQ_ELAUNCH every output of the call is unspecified.
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -82,8 +89,8 @@ typedef struct {
                                  [rows, cols/2]; 16-byte aligned                 */
     void *scales;             /* device u8, mxq_scale_bytes(rows, cols, fmt,
                                  layout) bytes; 16-byte aligned if swizzled     */
-    const float *global_scale;/* device fp32 scalar: NVFP4 encode scale g in
-                                 [2^-100, 2^100]; ignored for MXFP8             */
+    const float *global_scale;/* device fp32 scalar: NVFP4 encode scale g,
+                                 positive and finite; ignored for MXFP8         */
     int64_t rows;             /* 0 .. 2^31 - 128; 0 writes nothing             */
     int64_t src_ld;           /* row stride in elements: >= cols, multiple of 8 */
 } mxq_entry;
@@ -112,8 +119,10 @@ int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries
  * the fused gate/up slice has one amax].  Entry i belongs to scale slot
  * scale_slot[i]; a slot's amax is the max |x| over all of its entries and its
  * encode scale is
- *     g_s = 1 if amax_s = 0, else clamp(fp32(2688 / amax_s), 2^-100, 2^100)
- * (2688 = 448 * 6; the pages print no formula).  Every entry is then
+ *     g_s = 1 if amax_s = 0, else min(fp32(2688 / amax_s), FLT_MAX * 2^-9)
+ * (2688 = 448 * 6; the pages print no formula; the cap is the largest g for
+ * which every multiplier g / s_q, s_q >= 2^-9, is finite, and only amax below
+ * about 2^-107.6 reaches it).  Every entry is then
  * quantized exactly as mx_quant_grouped(MXQ_NVFP4, ...) with g = g_s of its
  * slot.  entries[i].global_scale is ignored.
  *   scale_slot        host int[n_entries], values in [0, n_slots), or NULL
@@ -148,7 +157,8 @@ int nvfp4_quant_grouped_auto(int layout, int64_t cols, const mxq_entry *entries,
  *                swizzled pads each expert to a multiple of 128 rows; an empty
  *                expert owns no bytes (16-byte aligned base if swizzled)
  *   row_amax     device fp32 [total_rows]: max_j |src[r, j]| (NULL to skip)
- * cols is a multiple of 16, at most 16384.  Any number of splits is allowed.
+ * cols is a multiple of 16, at most 16384.  Any number of splits is allowed,
+ * none included (then total_rows must be 0 and split_rows may be NULL).
  * 0 <= total_rows < 2^31, else MXQ_EINVAL; total_rows == 0 is MXQ_OK with no
  * launch.
  */
@@ -162,12 +172,13 @@ int nvfp4_quant_split(const void *src, int64_t total_rows, int64_t cols,
  * Description: row-scaled NVFP4 activations are quantized once and their
  * payload and row-scale metadata partitioned per expert; diagram: split
  * packed values and row amax].  Row r is quantized under its own encode scale
- *     g_r = 1                                   if a_r = 0,
- *     g_r = clamp(fp32(2688 / a_r), 2^-100, 2^100)  otherwise,
+ *     g_r = 1                                        if a_r = 0,
+ *     g_r = min(fp32(2688 / a_r), FLT_MAX * 2^-9)    otherwise,
  * a_r = max_j |src[r, j]| (2688 = 448 * 6: the row amax lands on the largest
  * E4M3 block scale times the largest E2M1 element; the pages print no
- * formula, this is the per-tensor convention applied per row, and the clamp
- * keeps every block multiplier finite and normal).  The decode scale of row r
+ * formula, this is the per-tensor convention applied per row; the cap keeps
+ * every block multiplier finite, and no lower bound is needed because
+ * 2688 / a_r >= 2688 / FLT_MAX keeps every multiplier normal).  The decode scale of row r
  * is 1 / g_r, which a consumer recomputes from row_amax.
  *   row_amax     device fp32 [total_rows], REQUIRED: a_r of every row
  * Everything else as nvfp4_quant_split (no global_scale).
@@ -237,7 +248,8 @@ int scale_swizzle(const void *linear, int64_t rows, int64_t sf_cols, void *swizz
 int64_t mxq_scale_bytes(int64_t rows, int64_t cols, int fmt, int layout);
 
 /* Byte offset of split i's scales in the bulk buffer (i == n_splits gives the
- * total size); -1 on bad arguments. */
+ * total size; split_rows may be NULL when n_splits == 0); -1 on bad
+ * arguments. */
 int64_t mxq_split_scale_offset(const int64_t *split_rows, int n_splits, int i, int64_t cols,
                                int fmt, int layout);
 

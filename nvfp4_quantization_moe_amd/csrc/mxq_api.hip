@@ -62,7 +62,7 @@ int64_t mxq_scale_bytes(int64_t rows, int64_t cols, int fmt, int layout) {
 
 int64_t mxq_split_scale_offset(const int64_t *split_rows, int n_splits, int i, int64_t cols,
                                int fmt, int layout) {
-    if (!split_rows || n_splits < 0 || i < 0 || i > n_splits) return -1;
+    if ((!split_rows && n_splits > 0) || n_splits < 0 || i < 0 || i > n_splits) return -1;
     if (!valid_fmt(fmt) || !valid_layout(layout) || cols <= 0 || cols % block_of(fmt) != 0)
         return -1;
     int64_t off = 0;
@@ -170,8 +170,8 @@ namespace {
 int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, int64_t cols,
                 const int64_t *split_rows, int n_splits, const float *global_scale,
                 void *payload, void *scales, float *row_amax, int layout, void *stream) {
-    if (!valid_layout(layout) || !split_rows || n_splits < 1 || total_rows < 0 ||
-        total_rows >= (int64_t)1 << 31)
+    if (!valid_layout(layout) || (!split_rows && n_splits > 0) || n_splits < 0 ||
+        total_rows < 0 || total_rows >= (int64_t)1 << 31)
         return MXQ_EINVAL;
     int64_t sum = 0;
     for (int i = 0; i < n_splits; ++i) {

@@ -140,46 +140,76 @@ __device__ __forceinline__ float div6(float a) {
     return __builtin_fmaf(r, r6, q);
 }
 
-// Element multiplier m = fp32(g / s_q) without a division per block.  Every
-// positive E4M3 value is s_q = d * 2^-k with d in 1..15 (d = 8 + mantissa for
-// exponent field e >= 1, k = 10 - e; d = mantissa, k = 9 for subnormals), and
-// rounding commutes with scaling by 2^k while the values stay normal, so
-// fp32(g / s_q) = fp32(g / d) * 2^k exactly.  The contract g in [2^-100,
-// 2^100] keeps g / d and g / s_q normal (so the flush of a non-normal
-// multiplier never applies).  Each wave computes the 15 quotients once, lane
-// d holding fp32(g / d) (IEEE division); a block fetches its quotient with a
-// cross-lane read, so every lane of the wave must take part in nv_scale.
-__device__ __forceinline__ float nv_wave_quot(float g) {
+// Element multiplier m = fp32(g / s_q), flushed to 0 when it is not a
+// normal fp32 number (subnormal, or infinite after overflow), for any
+// positive finite encode scale g.
+//
+// Quotient table (g >= 2^-117, every scale the library derives from an amax
+// and nearly every caller's): every positive E4M3 value is s_q = d * 2^-k
+// with d in 1..15 (d = 8 + mantissa for exponent field e >= 1, k = 10 - e;
+// d = mantissa, k = 9 for subnormals), and rounding commutes with scaling by
+// 2^k while the values stay normal, so fp32(g / s_q) = fp32(g / d) * 2^k.
+// For g >= 2^-117, g / 15 and g / 448 are normal, so that holds for every
+// code, and no multiplier is subnormal; a quotient that overflows does so in
+// both forms at the same threshold (round to 24 bits, then compare with
+// 2^128), so the ldexp gives inf exactly when the division does.  Each wave
+// computes the quotients once, lane d of every 16 holding fp32(g / d) (IEEE
+// division) and lane 0 holding 0 for code 0; a block fetches its quotient
+// with a cross-lane read, so every lane of the wave must take part.
+//
+// Below 2^-117 (a caller's scale; subnormal g included) the products can
+// leave the normal range, where that identity fails: each block then divides
+// (IEEE) and flushes a subnormal result.  g is uniform over the wave in
+// every kernel, so the two paths are a uniform branch.
+struct NvG {
+    float g;
+    float quot;  // table path: lane d of each 16 holds fp32(g / d), lane 0 holds 0
+    bool table;  // g >= 2^-117
+};
+
+__device__ __forceinline__ NvG nv_prepare(float g) {
     const int d = threadIdx.x & 15;
-    return g / (float)(d == 0 ? 1 : d);
+    NvG r;
+    r.g = g;
+    r.table = g >= 0x1p-117f;
+    r.quot = d == 0 ? 0.0f : g / (float)d;
+    return r;
 }
 
 // s = fp32(fp32(amax / 6) * g); code = E4M3(s), saturating at 448; multiplier
 // as above (0 for code 0, where s_q = 0).  All lanes of the wave must be
 // active.
-__device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, float g, float quot) {
-    const float s = div6(__uint_as_float(amax_bits << 16)) * g;
+__device__ __forceinline__ Nv4Scale nv_scale(uint32_t amax_bits, const NvG &G) {
+    const float s = div6(__uint_as_float(amax_bits << 16)) * G.g;
     Nv4Scale r;
     // v_cvt_scalef32_pk_fp8_f32 (scale 1.0) rounds to nearest even and keeps
     // values up to 448 exact to the rule; larger values are clamped first.
     const v2s k = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, __builtin_fminf(s, 448.0f),
                                                            0.0f, 1.0f, false);
     r.code = __builtin_bit_cast(uint32_t, k) & 0xFFu;
-    const uint32_t e = r.code >> 3, mant = r.code & 7u;
-    const int d = e == 0 ? (int)mant : (int)(8 + mant);
-    const int sh = e == 0 ? 9 : 10 - (int)e;
-    const float qd = __shfl(quot, d, 16);
-    r.mult = r.code == 0 ? 0.0f : __builtin_ldexpf(qd, sh);
+    float m;
+    if (G.table) {
+        const uint32_t e = r.code >> 3, mant = r.code & 7u;
+        const int d = e == 0 ? (int)mant : (int)(8 + mant);
+        const int sh = e == 0 ? 9 : 10 - (int)e;
+        m = __builtin_ldexpf(__shfl(G.quot, d, 16), sh);
+    } else {
+        m = G.g / e4m3_decode_pos(r.code);  // code 0: g / 0 = inf, flushed below
+        m = m >= 0x1p-126f ? m : 0.0f;
+    }
+    r.mult = m <= 0x1.fffffep+127f ? m : 0.0f;
     return r;
 }
 
 // NVFP4 encode scale from an amax a (a tensor's, a scale slot's or a row's):
 // 1 when a = 0, else fp32(2688 / a) (IEEE division; 2688 = 448 * 6 maps the
-// amax onto the largest block scale times the largest element) clamped to
-// [2^-100, 2^100], the range in which nv_scale's multipliers are exact.
+// amax onto the largest block scale times the largest element), capped at
+// FLT_MAX * 2^-9, the largest g for which g / 2^-9, the largest multiplier,
+// is finite.  No lower bound is needed: any finite a gives g >= 2688 /
+// FLT_MAX (about 2^-116.6), inside the quotient-table range.
 __device__ __forceinline__ float nv_encode_scale(float a) {
     if (a == 0.0f) return 1.0f;
-    return __builtin_fminf(__builtin_fmaxf(2688.0f / a, 0x1p-100f), 0x1p100f);
+    return __builtin_fminf(2688.0f / a, 0x1.fffffep+118f);
 }
 
 // Quantize 8 bf16 values with multiplier m; returns 4 bytes of packed E2M1
@@ -211,13 +241,13 @@ struct FmtTraits<MXQ_NVFP4> {
 };
 
 // Quantize one lane's 8 elements; the lanes of a block cooperate through DPP,
-// and NVFP4 fetches its multiplier quotient across the wave (nv_wave_quot),
-// so every lane of the wave must call it (lanes past the tensor pass zeros
+// and NVFP4 fetches its multiplier quotient across the wave (NvG), so every
+// lane of the wave must call it (lanes past the tensor pass zeros
 // and discard the result).  Returns the block's scale byte (every lane of the
 // block holds it) and the lane's payload: 8 bytes (MXFP8) or 4 bytes in pay.x
 // (NVFP4).
 template <int FMT>
-__device__ __forceinline__ uint32_t quant8(u32x4 v, float g, float quot, u32x2 &pay) {
+__device__ __forceinline__ uint32_t quant8(u32x4 v, const NvG &G, u32x2 &pay) {
     uint32_t a = amax_bits8(v);
     if constexpr (FMT == MXQ_MXFP8) {
         a = block_max4(a);
@@ -226,7 +256,7 @@ __device__ __forceinline__ uint32_t quant8(u32x4 v, float g, float quot, u32x2 &
         return c;
     } else {
         a = block_max2(a);
-        const Nv4Scale s = nv_scale(a, g, quot);
+        const Nv4Scale s = nv_scale(a, G);
         pay.x = nv_encode8(v, s.mult);
         pay.y = 0;
         return s.code;

@@ -54,7 +54,7 @@ void k_fused(const FusedArgs a) {
     const int part = w % WPR;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
     const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
-    const float quot = FMT == MXQ_NVFP4 ? nv_wave_quot(g) : 0.0f;
+    const NvG G = nv_prepare(g);
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     for (int k = threadIdx.x * 8; k < H; k += kNT * 8)  // H is a multiple of 16
         *reinterpret_cast<u32x4 *>(gamma_s + k) = *reinterpret_cast<const u32x4 *>(a.gamma + k);
@@ -122,7 +122,7 @@ void k_fused(const FusedArgs a) {
                     __builtin_nontemporal_store(nv, reinterpret_cast<u32x4 *>(a.norm_out + rb + col));
                 }
                 u32x2 pay;
-                const uint32_t code = quant8<FMT>(nv, g, quot, pay);  // whole wave
+                const uint32_t code = quant8<FMT>(nv, G, pay);  // whole wave
                 if (col < H) {
                     store_payload<FMT>(a.payload + (int64_t)r * payload_ld, col, pay);
                     if (leader) stage[q * a.sf_stride + col / Tr::kBlock] = (uint8_t)code;

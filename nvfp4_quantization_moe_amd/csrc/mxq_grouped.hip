@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
         const float g = FMT != MXQ_NVFP4 ? 0.0f
                         : AUTO ? nv_encode_scale(__uint_as_float(a.amax_bits[E.slot]))
                                : *E.g;
-        const float quot = FMT == MXQ_NVFP4 ? nv_wave_quot(g) : 0.0f;
+        const NvG G = nv_prepare(g);
 
         u32x4 v[kRowsPerWave];
 #pragma unroll
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
             uint32_t code = 0;  // rows and columns past the tensor stage zeros
             if (r < E.rows) {  // uniform: the whole wave quantizes
                 u32x2 pay;
-                const uint32_t c = quant8<FMT>(v[i], g, quot, pay);
+                const uint32_t c = quant8<FMT>(v[i], G, pay);
                 if (live_col) {
                     code = c;
                     store_payload<FMT>(E.payload + (int64_t)r * payload_ld, col, pay);

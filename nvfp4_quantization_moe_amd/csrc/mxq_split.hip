@@ -74,7 +74,7 @@ void k_split(const SplitArgs a) {
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
     const float g = (FMT == MXQ_NVFP4 && !ROWSC) ? *a.g : 0.0f;
-    const float quot = (FMT == MXQ_NVFP4 && !ROWSC) ? nv_wave_quot(g) : 0.0f;
+    const NvG G = nv_prepare(g);
     const int n_rows = a.row_off[a.n];
     const int n_row_units = (n_rows + kUnit - 1) / kUnit;
     const int tiles = a.sf_stride >> 2;
@@ -135,15 +135,15 @@ void k_split(const SplitArgs a) {
             for (int k = 0; k < NCH2; ++k) am = max(am, amax_bits8(cur[k]));
             return wave_max(am);
         };
-        // encode the half row in cur as row j of the unit under (gr, qr);
-        // whole wave.  am accumulates the half row's amax bits.
-        auto encode = [&](int j, float gr, float qr, uint32_t &am) {
+        // encode the half row in cur as row j of the unit under the encode
+        // scale Gr; whole wave.  am accumulates the half row's amax bits.
+        auto encode = [&](int j, const NvG &Gr, uint32_t &am) {
             uint8_t *pay_row = a.payload + (int64_t)(r0 + j) * payload_ld;
 #pragma unroll
             for (int k = 0; k < NCH2; ++k) {
                 const int col = (2 * k + half) * kChunk + lane * 8;
                 u32x2 pay;
-                const uint32_t code = quant8<FMT>(cur[k], gr, qr, pay);
+                const uint32_t code = quant8<FMT>(cur[k], Gr, pay);
                 if (col < a.cols) {
                     store_payload<FMT>(pay_row, col, pay);
                     if (!ROWSC) am = max(am, amax_bits8(cur[k]));
@@ -184,7 +184,7 @@ void k_split(const SplitArgs a) {
         if constexpr (!ROWSC) {
             for (int j = pair; j < n_live; j += kPairs) {
                 uint32_t am = 0;
-                encode(j, g, quot, am);
+                encode(j, G, am);
                 am = wave_max(am);
                 if (lane == 0) atomicMax(&row_max[j], am);
                 if (j + kPairs < n_live) load_row(j + kPairs, cur);
@@ -202,7 +202,7 @@ void k_split(const SplitArgs a) {
                     const float af = __uint_as_float(ra << 16);
                     const float gr = nv_encode_scale(af);
                     uint32_t unused = 0;
-                    encode(j, gr, nv_wave_quot(gr), unused);
+                    encode(j, nv_prepare(gr), unused);
                     if (a.row_amax && half == 0 && lane == 0) a.row_amax[r0 + j] = af;
                 }
                 if (j + kPairs < n_live) load_row(j + kPairs, cur);
@@ -272,7 +272,9 @@ static void split_layout(int layout, const SplitArgs &a, dim3 gd, size_t lds, hi
 
 hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,
                         hipStream_t s) {
-    const size_t lds = (size_t)kSplitUnitRows * a.sf_stride;
+    // the unit's codes; rounded up to 16 bytes, the granule of the zeroing
+    // stores of the padding columns
+    const size_t lds = ((size_t)kSplitUnitRows * a.sf_stride + 15) & ~(size_t)15;
     const dim3 gd((unsigned)(grid < 1 ? 1 : grid));
     if (fmt == MXQ_MXFP8)
         split_layout<MXQ_MXFP8, false>(layout, a, gd, lds, s);

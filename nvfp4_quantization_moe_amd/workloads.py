@@ -12,7 +12,8 @@ Recipes (every draw comes from a ``torch.Generator`` seeded as stated):
   * MoE layer weights (Qwen3-30B-A3B: gate_up [1536,2048], down [2048,768];
     Qwen3-235B-A22B: gate_up [3072,4096], down [4096,1536]): 128 experts per
     projection, N(0, std^2) (std 0.02 / 0.015), each entry times 50 with
-    probability 1e-4.
+    probability 1e-4; layer l of a model drawn from one generator seeded
+    2000 + l (30B-A3B) or 5000 + l (235B-A22B).
   * routed activation: bf16 [8192, 7168] N(0,1) times a per-token
     log-normal(0, 0.5) factor; 256 experts, 10 of them forced empty, the other
     split sizes drawn multinomially (uniform routing) over the tokens.
@@ -49,12 +50,13 @@ def small_grouped_experts(n_experts=8, rows=256, cols=512, seed=0, device="cpu")
 
 
 def expert_stack(n, rows, cols, std, seed, device="cpu", outlier_p=1e-4, outlier_mul=50.0,
-                 out=None):
+                 out=None, gen=None):
     """n same-shape expert weights as one bf16 [n, rows, cols] tensor.
 
-    Drawn on `device` with a generator of that device, in float32, then
-    rounded to bf16 (into `out` when given, so a stacking buffer is reused)."""
-    g = _gen(seed, device)
+    Drawn on `device` with a generator of that device (seeded `seed`, or
+    `gen` when given), in float32, then rounded to bf16 (into `out` when
+    given, so a stacking buffer is reused)."""
+    g = _gen(seed, device) if gen is None else gen
     if out is None:
         out = torch.empty(n, rows, cols, dtype=torch.bfloat16, device=device)
     for i in range(n):
@@ -64,6 +66,21 @@ def expert_stack(n, rows, cols, std, seed, device="cpu", outlier_p=1e-4, outlier
         x = torch.where(m, x * outlier_mul, x)
         out[i].copy_(x)
     return out
+
+
+def moe_layer(shapes, layer, base_seed, std, device="cpu", out=None):
+    """One MoE layer's expert weights, {projection: bf16 [N_EXPERTS, rows,
+    cols]} for the projections of `shapes` in order (gate_up, then down),
+    all drawn from one generator seeded base_seed + layer on `device` (the
+    Qwen3-235B-A22B layers use 5000 + l, std 0.015; the Qwen3-30B-A3B layers
+    2000 + l, std 0.02).  `out`, a dict of the same shapes, is reused when
+    given."""
+    g = _gen(base_seed + layer, device)
+    res = {}
+    for p, (r, c) in shapes.items():
+        res[p] = expert_stack(N_EXPERTS, r, c, std, None, device, out=None if out is None
+                              else out[p], gen=g)
+    return res
 
 
 def routed_activation(T=8192, H=7168, n_experts=256, n_empty=10, seed=3000, device="cpu"):
@@ -90,11 +107,3 @@ def epilogue_inputs(T, H=7168, seed=None, device="cpu"):
     gamma = (1.0 + 0.1 * torch.randn(H, generator=g)).to(torch.bfloat16)
     return x.to(device), res.to(device), gamma.to(device)
 
-
-def encode_scale_from_amax(amax: torch.Tensor) -> torch.Tensor:
-    """Caller-side NVFP4 second-level encode scale g = 2688 / amax (fp32).
-
-    2688 = 448 * 6 maps the tensor maximum onto the largest E4M3 block scale
-    times the largest E2M1 element; an all-zero tensor gets g = 1."""
-    a = amax.to(torch.float32)
-    return torch.where(a > 0, torch.full_like(a, 2688.0) / a, torch.ones_like(a))

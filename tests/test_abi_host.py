@@ -118,7 +118,13 @@ def _split(split, T=None, cols=64, src=A, g=A, pay=A, sc=A, amax=A, layout=1):
 def test_split_validation():
     assert _split([3, 4], T=8) == EINVAL           # sum != rows
     assert _split([3, -1, 4], T=6) == EINVAL       # negative split
-    assert _split([]) == EINVAL
+    assert _split([]) == OK                         # no splits, no rows: no launch
+    assert _split([], T=3) == EINVAL                # no splits cannot hold rows
+    L = mxq.lib()
+    assert L.nvfp4_quant_split(A, 0, 64, None, 0, A, A, A, A, 1, None) == OK
+    assert L.nvfp4_quant_split(A, 0, 64, None, 2, A, A, A, A, 1, None) == EINVAL
+    assert L.mxq_split_scale_offset(None, 0, 0, 64, 1, 1) == 0
+    assert L.mxq_split_scale_offset(None, 1, 0, 64, 1, 1) == -1
     assert _split([4], cols=40) == ESHAPE
     assert _split([4], cols=32768) == ESHAPE
     assert _split([4], layout=3) == EINVAL
@@ -146,7 +152,8 @@ def test_split_modes_validation():
     for f in (_split_rows, _split_mx):
         assert f([3, 4], T=8) == EINVAL
         assert f([3, -1, 4], T=6) == EINVAL
-        assert f([]) == EINVAL
+        assert f([]) == OK
+        assert f([], T=2) == EINVAL
         assert f([4], layout=2) == EINVAL
         assert f([4], cols=32768) == ESHAPE
         assert f([4], src=0) == EINVAL

@@ -314,3 +314,34 @@ def test_binding_rejects_small_outputs():
     # outputs on the host
     with pytest.raises(ValueError):
         mxq.mxfp8_quant_split(x, [64], mxq.LINEAR, payload=torch.empty(64 * 256, dtype=torch.uint8))
+
+
+# Caller encode scales outside the quotient-table range (g < 2^-117: the
+# division path) and scales whose multipliers overflow (flushed), through the
+# split and the fused epilogue.
+ODD_G = [2.0 ** -149, 12337 * 2.0 ** -149, 2.0 ** -126,
+         float(np.nextafter(np.float32(2.0 ** -117), np.float32(0))), 2.0 ** -117,
+         2.0 ** 126, float(np.finfo(np.float32).max)]
+
+
+@pytest.mark.parametrize("g", ODD_G, ids=[v.hex() for v in ODD_G])
+def test_split_and_fused_odd_caller_scales(orc, g):
+    T, H = 300, 1024
+    gen = torch.Generator().manual_seed(91)
+    # rows spread over 2^-120 .. 2^120 so that many block codes are met
+    x_cpu = (torch.randn(T, H, generator=gen) *
+             torch.exp2(torch.linspace(-120, 120, T))[:, None]).to(torch.bfloat16)
+    gd = torch.tensor([g], dtype=torch.float32, device=DEV)
+    split = [0, 7, 128, 0, 165]
+    for layout in (0, 1):
+        say("split with caller g", g.hex(), "layout", layout)
+        p, s, a, total = run_split(x_cpu.to(DEV), split, gd, layout)
+        op, os_, oa = orc.nvfp4_split(bf16_bits(x_cpu), split, float(np.float32(g)), layout)
+        assert np.array_equal(u8(p), op.ravel()) and np.array_equal(u8(s), os_)
+    xr, rr, gm = workloads.epilogue_inputs(64, H, seed=5)
+    say("fused NVFP4 with caller g", g.hex())
+    ro, no, fp, fs = mxq.rmsnorm_quant_fused(xr.to(DEV), rr.to(DEV), gm.to(DEV), 1e-6,
+                                            mxq.NVFP4, mxq.SWIZZLED, gd)
+    torch.cuda.synchronize()
+    op, os_ = orc.quantize(orc.NVFP4, orc.SWIZZLED, bf16_bits(no), g=float(np.float32(g)))
+    assert np.array_equal(u8(fp), op.ravel()) and np.array_equal(u8(fs), os_)

@@ -1,7 +1,7 @@
 """GPU parity of the row-scaled NVFP4 split and the MXFP8 split.
 
 Row-scaled: the hand-worked rows of tests/golden/row_scaled_rows.txt at
-several positions of a split; a hand split set whose rows span 2^-133 (clamped
+several positions of a split; a hand split set whose rows span 2^-133 (capped
 encode scale) to 2^127 with zero and negative-zero rows; the routed
 activation at full size ([8192,7168], 256 experts, 10 empty); every row width
 class the kernel instantiates; grid invariance.  MXFP8: the same hand split
@@ -57,8 +57,8 @@ def extreme_rows(T, H, seed):
     bits = bf16_bits(x.to(torch.bfloat16)).copy()
     bits[3] = 0x0000                       # zero row
     bits[5] = 0x8000                       # negative zeros
-    bits[7] = (np.arange(H) % 3 + 1)       # subnormals 2^-133..3*2^-133: g clamps at 2^100
-    bits[11] = 0x7F00                      # 2^127 everywhere: g clamps at 2^-100
+    bits[7] = (np.arange(H) % 3 + 1)       # subnormals 2^-133..3*2^-133: g capped at FLT_MAX*2^-9
+    bits[11] = 0x7F00                      # 2^127 everywhere: g = 21*2^-120, below the table range edge
     bits[11, ::7] = 0x7B80                 # ... with 2^120 entries
     bits[13, :] = 0x3F80
     bits[13, min(17, H - 1)] = 0x7F7F      # bf16 max in one place
