@@ -152,7 +152,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--cpu-experts", type=int, default=32,
-                    help="gate_up experts in the CPU oracle sample")
+                    help="gate_up experts in the single-thread MXFP8 CPU oracle sample")
+    ap.add_argument("--layers", type=int, default=8,
+                    help="resident Qwen3-235B-A22B layers the steps cycle through")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (hardware-counter calibration)")
     return ap.parse_args()
@@ -176,34 +178,48 @@ def main():
 
     E, G = workloads.N_EXPERTS, workloads.GROUP
     shapes = workloads.QWEN3_235B_A22B
-    log(f"[bench] generating one layer: {E} x gate_up {shapes['gate_up']} + {E} x down "
-        f"{shapes['down']} bf16")
-    buf = {p: workloads.expert_stack(E, r, c, std=0.015, seed=5000 + k, device=dev)
-           for k, (p, (r, c)) in enumerate(shapes.items())}
-    gsc = {p: caller_encode_scales(buf[p].float().abs().amax(dim=(1, 2))).contiguous()
-           for p in buf}
+    L = args.layers
+    log(f"[bench] generating {L} layers (seeds 5000 + l): {E} x gate_up {shapes['gate_up']} + "
+        f"{E} x down {shapes['down']} bf16 each, resident in HBM")
+    layers = [workloads.moe_layer(shapes, l, 5000, 0.015, device=dev) for l in range(L)]
+    gsc = [{p: caller_encode_scales(lay[p].float().abs().amax(dim=(1, 2))).contiguous()
+            for p in lay} for lay in layers]
     torch.cuda.synchronize()
 
-    # outputs: one payload buffer per format (both layouts write the same
-    # payload bytes), one scale buffer per (format, layout)
-    calls = []  # (fmt, layout, proj, GroupedCall)
-    alg_bytes = {}
+    # outputs, reused by every layer: one payload buffer per format and
+    # projection (both layouts write the same payload bytes), one scale
+    # buffer per (format, layout, projection)
+    outs = {}
     for fmt in (mxq.MXFP8, mxq.NVFP4):
         for proj, (r, c) in shapes.items():
             pw = c if fmt == mxq.MXFP8 else c // 2
-            pay = torch.empty(E, r, pw, dtype=torch.uint8, device=dev)
+            outs[(fmt, proj)] = torch.empty(E, r, pw, dtype=torch.uint8, device=dev)
             for layout in (mxq.LINEAR, mxq.SWIZZLED):
-                nsc = mxq.scale_bytes(r, c, fmt, layout)
-                sc = torch.empty(E, nsc, dtype=torch.uint8, device=dev)
-                for b in range(0, E, G):
-                    srcs = [buf[proj][b + i] for i in range(G)]
-                    gs = gsc[proj][b:b + G] if fmt == mxq.NVFP4 else None
-                    call = mxq.GroupedCall(fmt, layout, srcs, [pay[b + i] for i in range(G)],
-                                           [sc[b + i] for i in range(G)], gs)
-                    nbytes = G * (r * c * 2 + r * pw + nsc + (4 if fmt == mxq.NVFP4 else 0))
-                    calls.append((fmt, layout, proj, call, nbytes))
-                    alg_bytes[(fmt, layout)] = alg_bytes.get((fmt, layout), 0) + nbytes
-    step_bytes = sum(c[4] for c in calls)
+                outs[(fmt, layout, proj)] = torch.empty(E, mxq.scale_bytes(r, c, fmt, layout),
+                                                        dtype=torch.uint8, device=dev)
+    # calls[l]: layer l's 64 launches, (fmt, layout, proj, GroupedCall, bytes)
+    calls = []
+    alg_bytes = {}
+    for l, lay in enumerate(layers):
+        cl = []
+        for fmt in (mxq.MXFP8, mxq.NVFP4):
+            for proj, (r, c) in shapes.items():
+                pw = c if fmt == mxq.MXFP8 else c // 2
+                pay = outs[(fmt, proj)]
+                for layout in (mxq.LINEAR, mxq.SWIZZLED):
+                    sc = outs[(fmt, layout, proj)]
+                    nsc = sc.shape[1]
+                    for b in range(0, E, G):
+                        srcs = [lay[proj][b + i] for i in range(G)]
+                        gs = gsc[l][proj][b:b + G] if fmt == mxq.NVFP4 else None
+                        call = mxq.GroupedCall(fmt, layout, srcs, [pay[b + i] for i in range(G)],
+                                               [sc[b + i] for i in range(G)], gs)
+                        nbytes = G * (r * c * 2 + r * pw + nsc + (4 if fmt == mxq.NVFP4 else 0))
+                        cl.append((fmt, layout, proj, call, nbytes))
+                        if l == 0:
+                            alg_bytes[(fmt, layout)] = alg_bytes.get((fmt, layout), 0) + nbytes
+        calls.append(cl)
+    step_bytes = sum(c[4] for c in calls[0])
 
     import ctypes
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
@@ -212,21 +228,24 @@ def main():
     # back in runs of E/G; timing events sit only at run boundaries, so the
     # timed region carries 17 event records per step instead of two per
     # launch.  A launch's duration is its run's time over the run's launches
-    # (the gaps between them count against the kernel).
+    # (the gaps between them count against the kernel).  Step s quantizes
+    # layer s mod L.
     runs = []  # (first call index, end index)
-    for k in range(len(calls)):
-        if k == 0 or calls[k][:3] != calls[k - 1][:3]:
+    c0 = calls[0]
+    for k in range(len(c0)):
+        if k == 0 or c0[k][:3] != c0[k - 1][:3]:
             runs.append([k, k + 1])
         else:
             runs[-1][1] = k + 1
     n_ev = len(runs) + 1
 
-    def step(timer=None, base=0):
+    def step(s, timer=None, base=0):
+        cl = calls[s % L]
         for j, (k0, k1) in enumerate(runs):
             if timer is not None:
                 timer.record(base + j, stream)
             for k in range(k0, k1):
-                calls[k][3](stream)
+                cl[k][3](stream)
         if timer is not None:
             timer.record(base + len(runs), stream)
 
@@ -237,9 +256,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    log(f"[bench] warmup {args.warmup} steps ({len(calls)} launches/step)")
-    for _ in range(args.warmup):
-        step()
+    log(f"[bench] warmup {args.warmup} steps ({len(calls[0])} launches/step)")
+    for s in range(args.warmup):
+        step(s)
     torch.cuda.synchronize()
 
     timer = HipTimingEvents(n_ev * args.steps)
@@ -247,7 +266,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(timer, n_ev * s)
+        step(s, timer, n_ev * s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -260,14 +279,20 @@ def main():
     per = {}
     for s in range(args.steps):
         for j, (k0, k1) in enumerate(runs):
-            fmt, layout = calls[k0][0], calls[k0][1]
+            fmt, layout = c0[k0][0], c0[k0][1]
             ms = timer.elapsed_ms(n_ev * s + j, n_ev * s + j + 1)
             d = per.setdefault((fmt, layout), {"ms": 0.0, "n": 0, "bytes": 0})
             d["ms"] += ms
             d["n"] += k1 - k0
-            d["bytes"] += sum(calls[k][4] for k in range(k0, k1))
-    # spread of the per-step GPU time (events at each step's ends)
-    step_ms = sorted(timer.elapsed_ms(n_ev * s, n_ev * s + len(runs)) for s in range(args.steps))
+            d["bytes"] += sum(c0[k][4] for k in range(k0, k1))
+    # spread of the per-step GPU time (events at each step's ends), and the
+    # mean GPU time of each layer's steps
+    step_list = [timer.elapsed_ms(n_ev * s, n_ev * s + len(runs)) for s in range(args.steps)]
+    step_ms = sorted(step_list)
+    per_layer = {}
+    for s, ms in enumerate(step_list):
+        per_layer.setdefault(s % L, []).append(ms)
+    layer_ms = {str(l): round(sum(v) / len(v), 4) for l, v in sorted(per_layer.items())}
 
     def pct(p):
         return round(step_ms[min(len(step_ms) - 1, int(p * len(step_ms)))], 4)
@@ -301,18 +326,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16->mxfp8/nvfp4",
         "data": "synthetic",
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "step_ms_gpu": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
         "config": {
-            "workload": "Qwen3-235B-A22B-shaped MoE layer: 128 experts gate_up bf16 [3072,4096] "
-                        "+ 128 down bf16 [4096,1536], N(0,0.015^2) with 1e-4 outliers x50; "
-                        "MXFP8 and NVFP4, linear and swizzled scales, 16 experts per launch",
-            "experts": E, "experts_per_launch": G, "launches_per_step": len(calls),
+            "workload": f"Qwen3-235B-A22B-shaped MoE layers streamed: {L} layers (seeds 5000+l) "
+                        "of 128 experts gate_up bf16 [3072,4096] + 128 down bf16 [4096,1536], "
+                        "N(0,0.015^2) with 1e-4 outliers x50, resident in HBM; one step = one "
+                        "layer (step s quantizes layer s mod L) in MXFP8 and NVFP4, linear and "
+                        "swizzled scales, 16 experts per launch",
+            "layers": L, "experts": E, "experts_per_launch": G,
+            "launches_per_step": len(calls[0]),
             "alg_bytes_per_step": step_bytes,
             "alg_bytes_per_layer": {"mxfp8": alg_bytes[(0, 0)], "nvfp4": alg_bytes[(1, 0)]},
         },
+        "layer_ms_gpu": layer_ms,
         "per_kernel": per_kernel,
         "roofline": roofline,
     }
@@ -328,7 +357,7 @@ def main():
             cur = torch.cuda.current_stream(dev)
             for q in side:
                 q.wait_stream(cur)
-            for fmt, _, _, call, _ in calls:
+            for fmt, _, _, call, _ in calls[0]:
                 call(side_h[0 if fmt == mxq.MXFP8 else 1])
             for q in side:
                 cur.wait_stream(q)
@@ -343,7 +372,8 @@ def main():
                                    "GBps": round(step_bytes / t2 / 1e9, 1)}
         out["other_workloads"] = extra_workloads(torch, mxq, workloads, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(torch, buf["gate_up"], args.cpu_experts)
+        out["cpu_baseline"] = cpu_baseline(torch, layers[0]["gate_up"], gsc[0]["gate_up"],
+                                           args.cpu_experts)
     print(json.dumps(out), flush=True)
 
 
@@ -377,46 +407,49 @@ def extra_workloads(torch, mxq, workloads, dev):
     res["d2d_copy_4GiB"] = {"GBps": round(2 * n * 2 / t / 1e9, 1)}
     del a, b
 
-    # Qwen3-30B-A3B layer, MXFP8 swizzled: 16 grouped launches vs 256 per-expert launches
+    # Qwen3-30B-A3B model, MXFP8 swizzled: all 48 layers (seeds 2000 + l)
+    # resident and streamed, 16 grouped launches per layer; against 256
+    # per-expert launches per layer on the first 4 layers
     E, G = workloads.N_EXPERTS, workloads.GROUP
-    layer = {p: workloads.expert_stack(E, r, c, std=0.02, seed=2000, device=dev)
-             for p, (r, c) in workloads.QWEN3_30B_A3B.items()}
-    grouped, single = [], []
-    nbytes = 0
-    for p, (r, c) in workloads.QWEN3_30B_A3B.items():
-        pay = torch.empty(E, r, c, dtype=torch.uint8, device=dev)
-        sc = torch.empty(E, mxq.scale_bytes(r, c, 0, 1), dtype=torch.uint8, device=dev)
-        nbytes += E * (r * c * 3 + sc.shape[1])
-        for b0 in range(0, E, G):
-            grouped.append(mxq.GroupedCall(0, 1, [layer[p][b0 + i] for i in range(G)],
-                                           [pay[b0 + i] for i in range(G)],
-                                           [sc[b0 + i] for i in range(G)]))
-        for i in range(E):
-            single.append(mxq.GroupedCall(0, 1, [layer[p][i]], [pay[i]], [sc[i]]))
-    tg = timed(torch, lambda i: [c() for c in grouped], 10)
-    ts = timed(torch, lambda i: [c() for c in single], 10)
-    # the same 16 grouped launches alternating over two streams (default
-    # priority), so that one launch's ramp and tail overlap the other's work
-    side = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
-    side_h = [ctypes.c_void_p(q.cuda_stream) for q in side]
-
-    def two_streams(i):
-        cur = torch.cuda.current_stream(dev)
-        for q in side:
-            q.wait_stream(cur)
-        for k, c in enumerate(grouped):
-            c(side_h[k % 2])
-        for q in side:
-            cur.wait_stream(q)
-    t2 = timed(torch, two_streams, 10)
-    res["qwen3_30b_a3b_layer_mxfp8_swizzled"] = {
-        "alg_bytes": nbytes,
-        "grouped_16_launches_us": round(tg * 1e6, 1), "grouped_GBps": round(nbytes / tg / 1e9, 1),
-        "grouped_two_streams_us": round(t2 * 1e6, 1), "two_streams_GBps": round(nbytes / t2 / 1e9, 1),
-        "per_expert_256_launches_us": round(ts * 1e6, 1),
+    n_layers = 48
+    shapes30 = workloads.QWEN3_30B_A3B
+    log(f"[bench] generating {n_layers} Qwen3-30B-A3B layers")
+    layers30 = [workloads.moe_layer(shapes30, l, 2000, 0.02, device=dev) for l in range(n_layers)]
+    outs30 = {p: (torch.empty(E, r, c, dtype=torch.uint8, device=dev),
+                  torch.empty(E, mxq.scale_bytes(r, c, 0, 1), dtype=torch.uint8, device=dev))
+              for p, (r, c) in shapes30.items()}
+    nbytes = sum(E * (r * c * 3 + outs30[p][1].shape[1]) for p, (r, c) in shapes30.items())
+    grouped = []  # per layer and projection: one call of 8 launches
+    single = []   # per layer (first 4): its 256 launches
+    for l, lay in enumerate(layers30):
+        sl = []
+        for p in shapes30:
+            pay, sc = outs30[p]
+            srcs = [lay[p][i] for i in range(E)]
+            grouped.append(mxq.GroupedCall(0, 1, srcs, [pay[i] for i in range(E)],
+                                           [sc[i] for i in range(E)]))
+            if l < 4:
+                sl += [mxq.GroupedCall(0, 1, [lay[p][i]], [pay[i]], [sc[i]]) for i in range(E)]
+        if sl:
+            single.append(sl)
+    tg = timed(torch, lambda i: [c() for c in grouped], 1) / n_layers
+    ts = timed(torch, lambda i: [c() for sl in single for c in sl], 1) / len(single)
+    # the same calls through issue_overlapped: all 768 launches alternate over
+    # two side streams of default priority, joined to the calling stream
+    # before and after
+    t2 = timed(torch, lambda i: mxq.issue_overlapped(grouped), 1) / n_layers
+    per_launch = len(single[0]) - 2 * E // G
+    res["qwen3_30b_a3b_48_layers_mxfp8_swizzled"] = {
+        "layers": n_layers, "alg_bytes_per_layer": nbytes,
+        "grouped_16_launches_us_per_layer": round(tg * 1e6, 1),
+        "grouped_GBps": round(nbytes / tg / 1e9, 1),
+        "grouped_overlap_us_per_layer": round(t2 * 1e6, 1),
+        "overlap_GBps": round(nbytes / t2 / 1e9, 1),
+        "per_expert_256_launches_us_per_layer": round(ts * 1e6, 1),
         "per_expert_GBps": round(nbytes / ts / 1e9, 1),
-        "overhead_per_extra_launch_us": round((ts - tg) / (len(single) - len(grouped)) * 1e6, 2)}
-    del layer, grouped, single
+        "overhead_per_extra_launch_us": round((ts - tg) / per_launch * 1e6, 2)}
+    del layers30, outs30, grouped, single
+    torch.cuda.empty_cache()
 
     # the pages' flow for comparison: stack 16 experts into one buffer, then
     # quantize the stack as one tensor (MXFP8, swizzled; Qwen3-235B gate_up)
@@ -517,44 +550,82 @@ def extra_workloads(torch, mxq, workloads, dev):
                                             "GBps": round(3178496 / t / 1e9, 1)}
 
     # receiver-side scale conversion: the linear MXFP8 scales of one 16-expert
-    # gate_up launch (16 x [3072, 128] stacked) to the swizzled layout
+    # gate_up launch (16 x [3072, 128] stacked) to the swizzled layout, 48
+    # rotating inputs and outputs (604 MB, more than the 256 MB last-level
+    # cache holds), so each call reads and writes HBM
+    nrot = 48
     lin = [torch.randint(0, 255, (16 * 3072, 128), dtype=torch.uint8, device=dev)
-           for _ in range(4)]
-    outs = [torch.empty(16 * 3072 * 128, dtype=torch.uint8, device=dev) for _ in range(4)]
-    t = timed(torch, lambda i: mxq.scale_swizzle(lin[i % 4], outs[i % 4]), 50)
+           for _ in range(nrot)]
+    outs = [torch.empty(16 * 3072 * 128, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+    t = timed(torch, lambda i: mxq.scale_swizzle(lin[i % nrot], outs[i % nrot]), 2 * nrot)
     nb = 2 * 16 * 3072 * 128
-    res["scale_swizzle_49152x128"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
+    res["scale_swizzle_49152x128"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1),
+                                      "rotating_buffers": nrot}
+    del lin, outs
     return res
 
 
-def cpu_baseline(torch, gate_up, n_experts):
-    """The oracle, single-threaded, on the first n_experts gate_up experts
-    (MXFP8, swizzled): the same input bytes the GPU quantized."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(torch, gate_up, g_gate_up, n_experts):
+    """The oracle as it stands on the same input bytes the GPU quantized: the
+    first n_experts gate_up experts of layer 0, MXFP8 with swizzled scales,
+    single-threaded (the reported value); an NVFP4 sample (16 experts, their
+    per-expert encode scales); and MXFP8 on 64 experts with one oracle call
+    per expert on the host threads of the machine's CPU share for one GPU (the C
+    call releases the GIL)."""
     import numpy as np
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     oracle.lib()
     n_experts = min(n_experts, gate_up.shape[0])
-    host = gate_up[:n_experts].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    n_all = min(64, gate_up.shape[0])
+    host = gate_up[:n_all].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    g = g_gate_up.cpu().numpy()
     rows, cols = host.shape[1], host.shape[2]
+    mx_bytes = rows * cols * 3 + rows * cols // 32             # per expert, swizzled = linear here
+    nv_bytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4
     t0 = time.perf_counter()
     for i in range(n_experts):
         oracle.quantize(oracle.MXFP8, oracle.SWIZZLED, host[i])
     dt = time.perf_counter() - t0
-    nb = n_experts * (rows * cols * 3 + rows * cols // 32)
+    nb = n_experts * mx_bytes
     out = {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"{n_experts} gate_up experts bf16 [{rows},{cols}] of the same layer, "
-                     f"MXFP8 with swizzled scales ({nb} algorithmic bytes, {dt:.1f} s)"}
-    # the same oracle on one host thread per expert at a time (the C call
-    # releases the GIL), up to 16 threads: the machine's host cores at work
-    from concurrent.futures import ThreadPoolExecutor
-    n_threads = max(1, min(16, os.cpu_count() or 1))
+           "sample": f"{n_experts} gate_up experts bf16 [{rows},{cols}] of layer 0, MXFP8 with "
+                     f"swizzled scales ({nb} algorithmic bytes, {dt:.1f} s, one thread)",
+           "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+    n_nv = min(16, n_all)
+    t0 = time.perf_counter()
+    for i in range(n_nv):
+        oracle.quantize(oracle.NVFP4, oracle.SWIZZLED, host[i], g=float(g[i]))
+    dt = time.perf_counter() - t0
+    out["nvfp4"] = {"value": round(n_nv * nv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                    "sample": f"{n_nv} gate_up experts, NVFP4 swizzled, per-expert g "
+                              f"({n_nv * nv_bytes} algorithmic bytes, {dt:.1f} s)"}
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    n_threads = max(1, min(16, avail))
     t0 = time.perf_counter()
     with ThreadPoolExecutor(n_threads) as pool:
         list(pool.map(lambda i: oracle.quantize(oracle.MXFP8, oracle.SWIZZLED, host[i]),
-                      range(n_experts)))
+                      range(n_all)))
     dt = time.perf_counter() - t0
-    out["threaded"] = {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": n_threads,
-                       "seconds": round(dt, 2)}
+    out["threaded"] = {"value": round(n_all * mx_bytes / dt / 1e9, 4), "unit": "GB/s",
+                       "cores": n_threads, "cpus_available": avail, "seconds": round(dt, 2),
+                       "sample": f"{n_all} gate_up experts MXFP8 swizzled, one oracle call per "
+                                 f"expert on {n_threads} host threads (the CPU share of one GPU "
+                                 f"on the GPU box is 16 threads)"}
     return out
 
 

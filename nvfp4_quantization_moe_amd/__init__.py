@@ -19,7 +19,7 @@ __all__ = [
     "MXFP8", "NVFP4", "LINEAR", "SWIZZLED", "MAX_GROUP", "SPLIT_MODES", "MxqError",
     "mx_quant_grouped", "nvfp4_quant_grouped_auto", "nvfp4_quant_split",
     "nvfp4_quant_split_row_scaled", "mxfp8_quant_split", "rmsnorm_quant_fused", "scale_swizzle",
-    "GroupedCall", "GroupedAutoCall", "SplitCall", "FusedCall",
+    "GroupedCall", "GroupedAutoCall", "SplitCall", "FusedCall", "issue_overlapped",
     "scale_bytes", "split_scale_offset", "set_max_workgroups", "library_path", "lib",
 ]
 
@@ -178,7 +178,10 @@ class GroupedCall:
     loop, a benchmark): the tensors are checked and the C descriptor arrays
     packed at construction; each call is one C call per max_per_launch
     (default 16) experts on the current stream.  The tensors must stay alive
-    and keep their storage."""
+    and keep their storage.
+
+    To overlap the launches of many calls (a whole model's layers), pass
+    the calls to issue_overlapped()."""
 
     def __init__(self, fmt, layout, srcs, payloads=None, scales=None, global_scales=None,
                  max_per_launch=MAX_GROUP):
@@ -209,6 +212,55 @@ class GroupedCall:
             _check(L.mx_quant_grouped(self.fmt, self.layout, self.cols, ents, n, stream),
                    "mx_quant_grouped")
         return self.payloads, self.scales
+
+    def _launches(self):
+        L = lib()
+        for ents, n in self._batches:
+            yield lambda h, ents=ents, n=n: _check(
+                L.mx_quant_grouped(self.fmt, self.layout, self.cols, ents, n, h),
+                "mx_quant_grouped")
+
+
+_side_streams = {}
+
+
+def issue_overlapped(calls: Sequence["GroupedCall"], stream=None) -> None:
+    """Issue the launches of many prepacked grouped calls (a model's layers
+    and projections) alternately on two side streams of default priority,
+    so that one launch's ramp and tail overlap the next launch's work.
+
+    The side streams first wait for the calling stream (`stream`, a raw
+    hipStream_t handle, or the current stream), and the calling stream then
+    waits for both, so everything queued before the call is seen and
+    everything queued after it sees every output.  The calls' outputs must
+    be distinct, as within one call; the launches have no order among
+    themselves.  Worth it when launches are short (about 100 MB each or
+    less, as for a Qwen3-30B-A3B layer): there a launch's fixed ramp and
+    tail are a large part of its time."""
+    calls = list(calls)
+    if not calls:
+        return
+    dev = calls[0].device
+    if dev not in _side_streams:
+        pair = (torch.cuda.Stream(dev), torch.cuda.Stream(dev))  # default priority
+        _side_streams[dev] = (pair, [ctypes.c_void_p(q.cuda_stream) for q in pair])
+    side, handles = _side_streams[dev]
+    if stream is None:
+        cur = torch.cuda.current_stream(dev)
+    else:
+        h = stream.value if isinstance(stream, ctypes.c_void_p) else int(stream)
+        cur = torch.cuda.ExternalStream(h, device=dev)
+    for q in side:
+        q.wait_stream(cur)
+    k = 0
+    for c in calls:
+        if c.device != dev:
+            raise ValueError("issue_overlapped: all calls must be on one device")
+        for launch in c._launches():
+            launch(handles[k % 2])
+            k += 1
+    for q in side:
+        cur.wait_stream(q)
 
 
 class GroupedAutoCall:

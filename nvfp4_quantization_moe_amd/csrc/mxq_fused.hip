@@ -12,8 +12,11 @@ namespace mxq {
 
 // ---------------------------------------------------------------------------
 // WPR waves share each row, wave `part` holding the 512-column steps
-// WPR*k + part of it in registers.  gamma is staged in LDS once per
-// workgroup, then each unit's codes, one row per sf_stride bytes.
+// WPR*k + part of it in registers.  gamma is staged in LDS by the
+// workgroup's first unit with a live row, after that unit's row loads are
+// issued (measured 0.6-0.9 us faster at T = 1024-4096 than staging first);
+// units that hold only padding rows never load it.  Each unit's codes are
+// staged in LDS too, one row per sf_stride bytes.
 // ---------------------------------------------------------------------------
 
 // Copy n staged bytes to global memory with the whole workgroup (NT threads).
@@ -56,9 +59,7 @@ void k_fused(const FusedArgs a) {
     const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
     const NvG G = nv_prepare(g);
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
-    for (int k = threadIdx.x * 8; k < H; k += kNT * 8)  // H is a multiple of 16
-        *reinterpret_cast<u32x4 *>(gamma_s + k) = *reinterpret_cast<const u32x4 *>(a.gamma + k);
-    __syncthreads();
+    bool staged = false;  // gamma is in LDS (uniform)
     for (int lu0 = blockIdx.x; lu0 < a.total_units; lu0 += gridDim.x) {
         // the 8 rows whose swizzled codes share 16-byte lines on one XCD
         const int lu = LAYOUT == MXQ_SF_SWIZZLED && (int)gridDim.x == a.total_units
@@ -66,6 +67,8 @@ void k_fused(const FusedArgs a) {
                            : lu0;
         const int r = lu * RPU + q;
         const bool live = r < a.T;
+        const bool unit_live = lu * RPU < a.T;  // uniform: any live row in the unit
+        const bool stage_now = !staged && unit_live;
         const int64_t rb = (int64_t)r * H;
         u32x4 xv[NCHW];
         float acc = 0.0f;
@@ -79,6 +82,9 @@ void k_fused(const FusedArgs a) {
                     rv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.res + rb + col));
                 }
             }
+            if (stage_now)  // H is a multiple of 16
+                for (int k = threadIdx.x * 8; k < H; k += kNT * 8)
+                    *reinterpret_cast<u32x4 *>(gamma_s + k) = *reinterpret_cast<const u32x4 *>(a.gamma + k);
 #pragma unroll
             for (int k = 0; k < NCHW; ++k) {
                 const int col = (WPR * k + part) * kChunk + lane * 8;
@@ -99,9 +105,13 @@ void k_fused(const FusedArgs a) {
                 }
             }
             acc = wave_sum(acc);
+        } else if (stage_now) {  // a dead row of a unit with live rows
+            for (int k = threadIdx.x * 8; k < H; k += kNT * 8)
+                *reinterpret_cast<u32x4 *>(gamma_s + k) = *reinterpret_cast<const u32x4 *>(a.gamma + k);
         }
+        staged = staged || unit_live;
         if (lane == 0) red[w] = acc;
-        __syncthreads();
+        __syncthreads();  // the partial sums, and gamma in LDS
         if (live) {
             float ss = red[q * WPR];
 #pragma unroll

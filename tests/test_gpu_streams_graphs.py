@@ -136,3 +136,37 @@ def test_calls_from_several_host_threads(orc):
         assert d.max() <= 1  # N(0,1) inputs: no sign changes near zero matter here
         qp, qs = orc.quantize(k % 2, mxq.SWIZZLED, bf16_bits(no_gpu), g=80.0)
         assert np.array_equal(u8(p), qp.ravel()) and np.array_equal(u8(s), qs)
+
+
+def test_grouped_issue_overlapped(orc):
+    """issue_overlapped alternates the launches of several calls over two
+    side streams joined to the calling stream: the bytes equal the serial
+    calls', a late producer on the calling stream is seen, and a consumer
+    queued on the calling stream after it sees every output."""
+    xs_cpu = workloads.small_grouped_experts(n_experts=40, rows=128, cols=512, seed=21)
+    xs = [x.to(DEV) for x in xs_cpu]
+    serial = mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs)
+    halves = [mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs[:24]),
+              mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs[24:])]
+
+    def over():
+        mxq.issue_overlapped(halves)
+        return halves[0].payloads + halves[1].payloads, halves[0].scales + halves[1].scales
+    say("grouped overlap on two streams")
+    sp, ss = serial()
+    want = [u8(t).copy() for t in sp + ss]
+    late = [x.clone() for x in xs]
+    for x in xs:
+        x.zero_()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(20_000_000)      # the producer is late ...
+        for x, y in zip(xs, late):
+            x.copy_(y)                     # ... and restores the inputs
+        pays, scs = over()
+        copies = [t.clone() for t in pays + scs]  # a consumer on the calling stream
+    s.synchronize()
+    assert all(np.array_equal(u8(a), b) for a, b in zip(copies, want))
+    for i in (0, 17, 39):
+        p, sc = orc.quantize(orc.MXFP8, orc.SWIZZLED, bf16_bits(xs_cpu[i]))
+        assert np.array_equal(u8(pays[i]), p.ravel()) and np.array_equal(u8(scs[i]), sc)
