@@ -155,6 +155,8 @@ def parse():
                     help="gate_up experts in the single-thread MXFP8 CPU oracle sample")
     ap.add_argument("--layers", type=int, default=8,
                     help="resident Qwen3-235B-A22B layers the steps cycle through")
+    ap.add_argument("--c2-layers", type=int, default=48,
+                    help="Qwen3-30B-A3B layers streamed in the secondary workloads")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (hardware-counter calibration)")
     return ap.parse_args()
@@ -370,8 +372,9 @@ def main():
         t2 = (time.perf_counter() - t0) / args.steps
         out["step_two_streams"] = {"ms_per_step": round(t2 * 1e3, 4),
                                    "GBps": round(step_bytes / t2 / 1e9, 1)}
-        out["other_workloads"] = extra_workloads(torch, mxq, workloads, dev)
+        out["other_workloads"] = extra_workloads(torch, mxq, workloads, dev, args.c2_layers)
     if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (the oracle)")
         out["cpu_baseline"] = cpu_baseline(torch, layers[0]["gate_up"], gsc[0]["gate_up"],
                                            args.cpu_experts)
     print(json.dumps(out), flush=True)
@@ -394,7 +397,7 @@ def timed(torch, fn, iters, warm=3, reps=5):
     return sorted(per)[len(per) // 2]
 
 
-def extra_workloads(torch, mxq, workloads, dev):
+def extra_workloads(torch, mxq, workloads, dev, n_layers=48):
     import ctypes
     res = {}
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
@@ -411,7 +414,6 @@ def extra_workloads(torch, mxq, workloads, dev):
     # resident and streamed, 16 grouped launches per layer; against 256
     # per-expert launches per layer on the first 4 layers
     E, G = workloads.N_EXPERTS, workloads.GROUP
-    n_layers = 48
     shapes30 = workloads.QWEN3_30B_A3B
     log(f"[bench] generating {n_layers} Qwen3-30B-A3B layers")
     layers30 = [workloads.moe_layer(shapes30, l, 2000, 0.02, device=dev) for l in range(n_layers)]
@@ -428,7 +430,7 @@ def extra_workloads(torch, mxq, workloads, dev):
             srcs = [lay[p][i] for i in range(E)]
             grouped.append(mxq.GroupedCall(0, 1, srcs, [pay[i] for i in range(E)],
                                            [sc[i] for i in range(E)]))
-            if l < 4:
+            if l < min(4, n_layers):
                 sl += [mxq.GroupedCall(0, 1, [lay[p][i]], [pay[i]], [sc[i]]) for i in range(E)]
         if sl:
             single.append(sl)
@@ -451,6 +453,7 @@ def extra_workloads(torch, mxq, workloads, dev):
     del layers30, outs30, grouped, single
     torch.cuda.empty_cache()
 
+    log("[bench] stacking copy against the descriptor table")
     # the pages' flow for comparison: stack 16 experts into one buffer, then
     # quantize the stack as one tensor (MXFP8, swizzled; Qwen3-235B gate_up)
     r, c = workloads.QWEN3_235B_A22B["gate_up"]
@@ -472,6 +475,7 @@ def extra_workloads(torch, mxq, workloads, dev):
         "stack_then_quantize_us": round(ts * 1e6, 1), "quantize_stacked_only_us": round(tq * 1e6, 1)}
     del stack, experts, flat, in_place, one_tensor
 
+    log("[bench] encode scales from the data")
     # NVFP4 with encode scales from the data, same call (amax pass + quantize):
     # one Qwen3-235B-A22B gate_up launch of 16 experts, swizzled
     r, c = workloads.QWEN3_235B_A22B["gate_up"]
@@ -496,6 +500,7 @@ def extra_workloads(torch, mxq, workloads, dev):
         "torch_amax_then_grouped_us": round(tt * 1e6, 1)}
     del stack, auto, plain
 
+    log("[bench] routed activation split")
     # routed activation split, 8 rotating input copies (> MALL): NVFP4 with one
     # encode scale, row-scaled NVFP4, MXFP8; linear and swizzled scales
     x, split = workloads.routed_activation()
@@ -518,6 +523,7 @@ def extra_workloads(torch, mxq, workloads, dev):
     res["split_8192x7168_256experts"] = splits
     del xs
 
+    log("[bench] fused epilogue sweep")
     # fused residual + RMSNorm + quantize (swizzled), MXFP8 and NVFP4, with the
     # same-run e4m3 cast reference
     for fmt, fname in ((0, "mxfp8"), (1, "nvfp4")):
@@ -542,6 +548,7 @@ def extra_workloads(torch, mxq, workloads, dev):
             sweep[str(T)] = entry
         res[f"fused_rmsnorm_{fname}_H7168"] = sweep
 
+    log("[bench] small grouped case, scale swizzle")
     # small grouped case: 8 x [256,512] MXFP8 linear (launch-bound)
     xs8 = [x.to(dev) for x in workloads.small_grouped_experts(seed=0)]
     call = mxq.GroupedCall(0, 0, xs8)

@@ -35,7 +35,7 @@ CMD_KT = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --o
           "-d $OUT/prof_kt -o kt -- python3 $REPO/bench.py --steps 5 --warmup 1 --no-cpu-baseline")
 CMD_F = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
          "-d $OUT/prof_fetch -o f -- python3 $REPO/bench.py --steps 2 --warmup 1 "
-         "--no-cpu-baseline --calib-copy")
+         "--no-cpu-baseline --calib-copy --c2-layers 2")
 CMD_W = CMD_F.replace("FETCH_SIZE", "WRITE_SIZE").replace("prof_fetch", "prof_write").replace(
     "-o f ", "-o w ")
 HDR = ("Commands (`$REPO` is the repository root, `$OUT` an output folder; each counter in a run "
@@ -145,6 +145,25 @@ def write_valu_summary(valu_csv, ms_csv, out_dir):
             "within 3 % of MXFP8's bandwidth.\n")
 
 
+def write_stats_summary(stats_csv, out_dir):
+    """rocprofv3's own --stats summary of the kernel-trace run (all dispatches
+    of a kernel name together, every workload of the run included)."""
+    with open(stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    lines = [f"| `{r['Name'][:90]}` | {int(r['Calls']):,} | {float(r['AverageNs']) / 1e3:,.2f} | "
+             f"{float(r['MinNs']) / 1e3:,.2f} | {float(r['MaxNs']) / 1e3:,.2f} | {r['Percentage']} |"
+             for r in rows]
+    with open(os.path.join(out_dir, "rocprofv3_kernel_stats_bench.md"), "w") as fh:
+        fh.write("# rocprofv3 --kernel-trace --stats summary of bench.py (kt_kernel_stats.csv), "
+                 "MI355X\n\nCommand (`$REPO` is the repository root, `$OUT` an output folder):\n\n"
+                 "```\n" + CMD_KT + "\n```\n\n"
+                 "One row per kernel name over every dispatch of the run (the layer steps and the "
+                 "secondary workloads together), as rocprofv3 wrote it; the per-launch-shape "
+                 "figures are in the k_*.md summaries.\n\n"
+                 "| kernel | calls | avg us | min us | max us | % of kernel time |\n"
+                 "|---|---|---|---|---|---|\n" + "\n".join(lines) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("dir", help="folder holding prof_kt, prof_fetch and prof_write")
@@ -215,8 +234,9 @@ def main(argv=None):
     write_md("k_grouped_qwen3_235b_layer.md",
              "k_grouped -- Qwen3-235B-A22B-shaped MoE layer, 16 experts per launch, MI355X",
              "## Kernel trace (per dispatch, from kt_kernel_trace.csv)\n\n"
-             "gate_up = 16 x bf16 [3072,4096], down = 16 x bf16 [4096,1536]; 6 dispatches each "
-             "(1 warm-up + 5 timed steps).  GB/s = algorithmic bytes / average duration.\n\n"
+             "gate_up = 16 x bf16 [3072,4096], down = 16 x bf16 [4096,1536]; 6 steps of 8 "
+             "dispatches each (1 warm-up + 5 timed steps, each step one of the 8 streamed layers).  "
+             "GB/s = algorithmic bytes / average duration.\n\n"
              "| kernel | launch | n | avg us | min us | max us | GB/s |\n|---|---|---|---|---|---|---|\n"
              + "\n".join(lines_t) + "\n\n"
              "The benchmark's `per_kernel.avg_us` comes from HIP events at the boundaries of each "
@@ -228,8 +248,9 @@ def main(argv=None):
              "|---|---|---|---|---|---|---|\n" + "\n".join(lines_c) + "\n")
 
     # ------------------------------------- grouped against per-expert dispatch
-    # Qwen3-30B-A3B layer, MXFP8 swizzled: each timed call issues 8 gate_up + 8
-    # down grouped launches, or 128 + 128 single-expert launches, back to back
+    # Qwen3-30B-A3B layers, MXFP8 swizzled: each layer is 8 gate_up + 8 down
+    # grouped launches, or 128 + 128 single-expert launches, back to back; the
+    # serial grouped passes over the 48 layers come first
     rows_l, spans = [], {}
     for kind, per in (("grouped", 16), ("per-expert", 1)):
         grids = {p: per * (-(-r // 128) * 128 // 16) * (-(-c // 512)) * 256
@@ -265,8 +286,8 @@ def main(argv=None):
              "kernel time: the fixed ramp and tail of a launch, which grouping pays once per 16 "
              "experts.  Kernel tracing adds its own host-side cost to every launch, so the traced "
              f"span ({(se - sg) / (ne - ng) / 1e3:.2f} us per extra launch) overstates the gap; "
-             "bench.py reports the untraced layer times "
-             "(`other_workloads.qwen3_30b_a3b_layer_mxfp8_swizzled`).\n")
+             "bench.py reports the untraced layer times over all 48 layers "
+             "(`other_workloads.qwen3_30b_a3b_48_layers_mxfp8_swizzled`).\n")
 
     # ------------------------------------------------ encode scales from data
     r, c = shapes["gate_up"]
@@ -374,8 +395,8 @@ def main(argv=None):
     write_md("k_swizzle_49152x128.md",
              "k_swizzle -- linear MXFP8 scales of a 16-expert Qwen3-235B-A22B gate_up launch "
              "(u8 [49152,128]) to the swizzled 128x4 layout, MI355X",
-             "Algorithmic bytes: the linear matrix in, the swizzled matrix out.  4 input/output "
-             "pairs rotate.\n\n" + calib + "\n"
+             "Algorithmic bytes: the linear matrix in, the swizzled matrix out.  48 input/output "
+             "pairs rotate (604 MB, more than the 256 MB last-level cache).\n\n" + calib + "\n"
              "| kernel | n | avg us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
              "|---|---|---|---|---|---|---|---|\n"
              f"| k_swizzle | {len(dur)} | {avg(dur) / 1e3:,.2f} | {alg:,} | {alg / avg(dur):,.0f} | "
@@ -391,6 +412,10 @@ def main(argv=None):
     ms_csv = os.path.join(d, "pmc_ms", "m_counter_collection.csv")
     if os.path.exists(valu_csv) and os.path.exists(ms_csv):
         write_valu_summary(valu_csv, ms_csv, out_dir)
+
+    stats_csv = os.path.join(d, "prof_kt", "kt_kernel_stats.csv")
+    if os.path.exists(stats_csv):
+        write_stats_summary(stats_csv, out_dir)
 
     with open(os.path.join(out_dir, "hbm_traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
