@@ -55,7 +55,8 @@
  * fails it returns a nonzero mxq_status, launches nothing and writes nothing.
  * MXQ_ELAUNCH reports a kernel launch that the HIP runtime rejected after
  * validation passed.  A call that issues several launches
- * (nvfp4_quant_grouped_auto; a split with more than 256 non-empty experts)
+ * (mx_quant_grouped_batch; nvfp4_quant_grouped_auto; a split with more than
+ * 256 non-empty experts)
  * may then have enqueued the launches before the failed one, so after
  * MXQ_ELAUNCH every output of the call is unspecified.
  */
@@ -111,6 +112,34 @@ typedef struct {
  */
 int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries, int n_entries,
                      void *stream);
+
+/*
+ * mx_quant_grouped_batch -- mx_quant_grouped over any number of entries that
+ * share `cols` (a model's experts of one projection, say): ceil(n_entries /
+ * per_launch) launches of up to per_launch (1..16) entries, in entry order,
+ * on `stream` [RL-3804, Summary: batches of at most 16 experts; Why: the
+ * per-launch cost is what batching removes].  The bytes are those of
+ * mx_quant_grouped on each batch.
+ *   flags  0, or MXQ_CHAIN: every launch after the first is dispatched with
+ *          HIP's any-order launch (the barrier bit of its dispatch packet
+ *          clear), so it may start while the previous launch drains, hiding
+ *          that launch's ramp and tail.  The first launch is ordinary, so the
+ *          whole call still follows everything queued before it, and work
+ *          queued after the call still follows all of its launches.  The
+ *          launches of one call read only inputs and write only distinct
+ *          outputs (outputs must not alias inputs or each other, across the
+ *          whole call), so their order does not matter.  On a stream being
+ *          captured into a graph the launches are ordinary.  Measured: a
+ *          Qwen3-30B-A3B-shaped layer's 2 x 8 launches of 76-153 MB take
+ *          348 -> 328 us; launches of 300 MB and more gain nothing (about 1 %
+ *          slower), so leave it off there.
+ * Every batch is validated before the first launch; errors as
+ * mx_quant_grouped, plus MXQ_EINVAL for n_entries < 1, per_launch outside
+ * [1, 16] or an unknown flag.
+ */
+#define MXQ_CHAIN 1u
+int mx_quant_grouped_batch(int fmt, int layout, int64_t cols, const mxq_entry *entries,
+                           int n_entries, int per_launch, unsigned flags, void *stream);
 
 /*
  * nvfp4_quant_grouped_auto -- mx_quant_grouped for NVFP4 with the encode

@@ -19,13 +19,14 @@ __all__ = [
     "MXFP8", "NVFP4", "LINEAR", "SWIZZLED", "MAX_GROUP", "SPLIT_MODES", "MxqError",
     "mx_quant_grouped", "nvfp4_quant_grouped_auto", "nvfp4_quant_split",
     "nvfp4_quant_split_row_scaled", "mxfp8_quant_split", "rmsnorm_quant_fused", "scale_swizzle",
-    "GroupedCall", "GroupedAutoCall", "SplitCall", "FusedCall", "issue_overlapped",
+    "GroupedCall", "GroupedAutoCall", "SplitCall", "FusedCall", "CHAIN",
     "scale_bytes", "split_scale_offset", "set_max_workgroups", "library_path", "lib",
 ]
 
 MXFP8, NVFP4 = 0, 1
 LINEAR, SWIZZLED = 0, 1
 MAX_GROUP = 16
+CHAIN = 1  # mx_quant_grouped_batch flag: launches after the first dispatched any-order
 _BLOCK = {MXFP8: 32, NVFP4: 16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
         i64, vp, ci, cf = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         sigs = {
             "mx_quant_grouped": (ci, [ci, ci, i64, ctypes.POINTER(_Entry), ci, vp]),
+            "mx_quant_grouped_batch": (ci, [ci, ci, i64, ctypes.POINTER(_Entry), ci, ci,
+                                            ctypes.c_uint, vp]),
             "nvfp4_quant_grouped_auto": (ci, [ci, i64, ctypes.POINTER(_Entry), ci,
                                               ctypes.POINTER(ci), ci, vp, vp, vp]),
             "nvfp4_quant_split": (ci, [vp, i64, i64, ctypes.POINTER(i64), ci, vp, vp, vp, vp,
@@ -150,117 +153,49 @@ def mx_quant_grouped(fmt: int, layout: int, srcs: Sequence[torch.Tensor],
     payload [rows, cols] (MXFP8) or [rows, cols/2] (NVFP4); scales flat,
     scale_bytes(rows, cols, fmt, layout) bytes.  The bytes do not depend on
     max_per_launch."""
-    per = _per_launch(max_per_launch)
     srcs = list(srcs)
     if not srcs:
+        _per_launch(max_per_launch)
         return [], []
-    payloads, scales = _grouped_outputs(fmt, layout, srcs, payloads, scales, global_scales)
-    cols = srcs[0].shape[1]
-    dev = srcs[0].device
-    stream = _stream(dev)
-    for b in range(0, len(srcs), per):
-        n = min(per, len(srcs) - b)
-        ents = (_Entry * n)()
-        for j in range(n):
-            i = b + j
-            s = srcs[i]
-            gs = None if fmt == MXFP8 else global_scales.data_ptr() + 4 * i
-            ents[j] = _Entry(s.data_ptr(), payloads[i].data_ptr(), scales[i].data_ptr(), gs,
-                             s.shape[0], _row_stride(s))
-        _check(lib().mx_quant_grouped(fmt, layout, cols, ents, n, stream), "mx_quant_grouped")
-    return payloads, scales
+    call = GroupedCall(fmt, layout, srcs, payloads, scales, global_scales, max_per_launch)
+    return call()
 
 
 class GroupedCall:
-    """mx_quant_grouped with its descriptor tables built once.
+    """Grouped quantization of same-width experts with the C descriptor array
+    packed once: one mx_quant_grouped_batch call of max_per_launch (1..16)
+    experts per launch on the current stream.
 
     For callers that issue the same grouped quantization repeatedly (a refit
-    loop, a benchmark): the tensors are checked and the C descriptor arrays
-    packed at construction; each call is one C call per max_per_launch
-    (default 16) experts on the current stream.  The tensors must stay alive
-    and keep their storage.
-
-    To overlap the launches of many calls (a whole model's layers), pass
-    the calls to issue_overlapped()."""
+    loop, a benchmark).  The tensors must stay alive and keep their storage.
+    chain=True passes MXQ_CHAIN: launches after the first may start while the
+    previous one drains (measured 348 -> 328 us on a Qwen3-30B-A3B layer's
+    2 x 8 launches; no gain for launches of 300 MB and more)."""
 
     def __init__(self, fmt, layout, srcs, payloads=None, scales=None, global_scales=None,
-                 max_per_launch=MAX_GROUP):
-        per = _per_launch(max_per_launch)
+                 max_per_launch=MAX_GROUP, chain=False):
+        self.per = _per_launch(max_per_launch)
         self.fmt, self.layout = fmt, layout
+        self.flags = CHAIN if chain else 0
         self.payloads, self.scales = _grouped_outputs(fmt, layout, srcs, payloads, scales,
                                                       global_scales)
         self.srcs = list(srcs)
         self.global_scales = global_scales
         self.cols = self.srcs[0].shape[1]
         self.device = self.srcs[0].device
-        self._batches = []
-        for b in range(0, len(self.srcs), per):
-            n = min(per, len(self.srcs) - b)
-            ents = (_Entry * n)()
-            for j in range(n):
-                i = b + j
-                s = self.srcs[i]
-                gs = None if fmt == MXFP8 else global_scales.data_ptr() + 4 * i
-                ents[j] = _Entry(s.data_ptr(), self.payloads[i].data_ptr(),
-                                 self.scales[i].data_ptr(), gs, s.shape[0], _row_stride(s))
-            self._batches.append((ents, n))
+        n = len(self.srcs)
+        self._ents = (_Entry * n)()
+        for i, s in enumerate(self.srcs):
+            gs = None if fmt == MXFP8 else global_scales.data_ptr() + 4 * i
+            self._ents[i] = _Entry(s.data_ptr(), self.payloads[i].data_ptr(),
+                                   self.scales[i].data_ptr(), gs, s.shape[0], _row_stride(s))
 
     def __call__(self, stream: Optional[ctypes.c_void_p] = None):
         stream = _stream(self.device) if stream is None else stream
-        L = lib()
-        for ents, n in self._batches:
-            _check(L.mx_quant_grouped(self.fmt, self.layout, self.cols, ents, n, stream),
-                   "mx_quant_grouped")
+        _check(lib().mx_quant_grouped_batch(self.fmt, self.layout, self.cols, self._ents,
+                                            len(self.srcs), self.per, self.flags, stream),
+               "mx_quant_grouped_batch")
         return self.payloads, self.scales
-
-    def _launches(self):
-        L = lib()
-        for ents, n in self._batches:
-            yield lambda h, ents=ents, n=n: _check(
-                L.mx_quant_grouped(self.fmt, self.layout, self.cols, ents, n, h),
-                "mx_quant_grouped")
-
-
-_side_streams = {}
-
-
-def issue_overlapped(calls: Sequence["GroupedCall"], stream=None) -> None:
-    """Issue the launches of many prepacked grouped calls (a model's layers
-    and projections) alternately on two side streams of default priority,
-    so that one launch's ramp and tail overlap the next launch's work.
-
-    The side streams first wait for the calling stream (`stream`, a raw
-    hipStream_t handle, or the current stream), and the calling stream then
-    waits for both, so everything queued before the call is seen and
-    everything queued after it sees every output.  The calls' outputs must
-    be distinct, as within one call; the launches have no order among
-    themselves.  Worth it when launches are short (about 100 MB each or
-    less, as for a Qwen3-30B-A3B layer): there a launch's fixed ramp and
-    tail are a large part of its time."""
-    calls = list(calls)
-    if not calls:
-        return
-    dev = calls[0].device
-    if dev not in _side_streams:
-        pair = (torch.cuda.Stream(dev), torch.cuda.Stream(dev))  # default priority
-        _side_streams[dev] = (pair, [ctypes.c_void_p(q.cuda_stream) for q in pair])
-    side, handles = _side_streams[dev]
-    if stream is None:
-        cur = torch.cuda.current_stream(dev)
-    else:
-        h = stream.value if isinstance(stream, ctypes.c_void_p) else int(stream)
-        cur = torch.cuda.ExternalStream(h, device=dev)
-    for q in side:
-        q.wait_stream(cur)
-    k = 0
-    for c in calls:
-        if c.device != dev:
-            raise ValueError("issue_overlapped: all calls must be on one device")
-        for launch in c._launches():
-            launch(handles[k % 2])
-            k += 1
-    for q in side:
-        cur.wait_stream(q)
 
 
 class GroupedAutoCall:

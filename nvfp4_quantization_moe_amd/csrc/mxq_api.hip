@@ -115,6 +115,11 @@ int pack_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries, in
         if (units >= (int64_t)1 << 31) return MXQ_ESHAPE;
     }
     a.total_units = (int32_t)units;
+    // every entry the same number of units: the kernel finds a unit's entry
+    // by one division
+    a.uniform_units = units > 0 && units % n_entries == 0 ? (int32_t)(units / n_entries) : 0;
+    for (int i = 0; i < n_entries && a.uniform_units; ++i)
+        if (a.e[i].unit_begin != i * a.uniform_units) a.uniform_units = 0;
     return MXQ_OK;
 }
 
@@ -131,6 +136,39 @@ int mx_quant_grouped(int fmt, int layout, int64_t cols, const mxq_entry *entries
     hipError_t err =
         launch_grouped(fmt, layout, false, a, grid_for(a.total_units), (hipStream_t)stream);
     return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;
+}
+
+int mx_quant_grouped_batch(int fmt, int layout, int64_t cols, const mxq_entry *entries,
+                           int n_entries, int per_launch, unsigned flags, void *stream) {
+    if (n_entries < 1 || per_launch < 1 || per_launch > MXQ_MAX_GROUP || !entries ||
+        (flags & ~(unsigned)MXQ_CHAIN) != 0)
+        return MXQ_EINVAL;
+    // every launch's entries are checked before the first launch
+    GroupArgs a;
+    for (int b = 0; b < n_entries; b += per_launch) {
+        const int n = n_entries - b < per_launch ? n_entries - b : per_launch;
+        const int st = pack_grouped(fmt, layout, cols, entries + b, n, fmt == MXQ_NVFP4, a);
+        if (st != MXQ_OK) return st;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    // a stream being captured into a graph gets ordinary launches
+    bool chain = (flags & MXQ_CHAIN) != 0;
+    if (chain) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+            chain = false;
+    }
+    bool first = true;  // the first launch keeps the stream's order
+    for (int b = 0; b < n_entries; b += per_launch) {
+        const int n = n_entries - b < per_launch ? n_entries - b : per_launch;
+        pack_grouped(fmt, layout, cols, entries + b, n, fmt == MXQ_NVFP4, a);
+        if (a.total_units == 0) continue;
+        if (launch_grouped(fmt, layout, false, a, grid_for(a.total_units), s, chain && !first) !=
+            hipSuccess)
+            return MXQ_ELAUNCH;
+        first = false;
+    }
+    return MXQ_OK;
 }
 
 int nvfp4_quant_grouped_auto(int layout, int64_t cols, const mxq_entry *entries, int n_entries,

@@ -62,7 +62,7 @@ void k_fused(const FusedArgs a) {
     bool staged = false;  // gamma is in LDS (uniform)
     for (int lu0 = blockIdx.x; lu0 < a.total_units; lu0 += gridDim.x) {
         // the 8 rows whose swizzled codes share 16-byte lines on one XCD
-        const int lu = LAYOUT == MXQ_SF_SWIZZLED && (int)gridDim.x == a.total_units
+        const int lu = LAYOUT == MXQ_SF_SWIZZLED && xcd_grouping_holds(gridDim.x, a.total_units)
                            ? xcd_grouped_unit<8 / RPU>(lu0, a.total_units)
                            : lu0;
         const int r = lu * RPU + q;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void k_swizzle(const SwizzleArgs a) {
     // once (measured 2.0x -> 1.02x the input on 128-column rows)
     const int g = groups < 16 ? (int)groups : 16;
     for (int64_t u0 = blockIdx.x; u0 < n_units; u0 += gridDim.x) {
-        const int64_t u = (int64_t)gridDim.x == n_units ? xcd_grouped_unit(u0, n_units, g) : u0;
+        const int64_t u = xcd_grouping_holds(gridDim.x, n_units) ? xcd_grouped_unit(u0, n_units, g) : u0;
         const int64_t band = u / groups, t0 = (u - band * groups) * nt;
         // kBatch loads in flight per thread before any LDS write
         constexpr int kBatch = 8;

@@ -27,6 +27,8 @@
 // and no inter-workgroup ordering: every byte has one writer, and the bytes
 // do not depend on the grid size.  (k_amax, for encode scales from the data,
 // folds each workgroup's maximum into its slot with one atomic max.)
+#include <hip/hip_ext.h>
+
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
@@ -65,11 +67,17 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupArgs a) {
     for (int u0 = blockIdx.x; u0 < a.total_units; u0 += gridDim.x) {
         // linear: 8 consecutive units (the column chunks of a row group) share
         // 128-byte scale lines; meeting in one L2 merges their partial lines
-        const int u = LAYOUT == MXQ_SF_LINEAR && (int)gridDim.x == a.total_units
+        const int u = LAYOUT == MXQ_SF_LINEAR && xcd_grouping_holds(gridDim.x, a.total_units)
                           ? xcd_grouped_unit<8>(u0, a.total_units)
                           : u0;
+        // the unit's entry: one scalar division when every entry has the same
+        // number of units (every launch of a model layer; 0.5-1.2 us per
+        // launch faster than the walk), else a walk of the table
         int ei = 0;
-        while (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) ++ei;
+        if (a.uniform_units > 0)
+            ei = u / a.uniform_units;
+        else
+            while (ei + 1 < a.n && u >= a.e[ei + 1].unit_begin) ++ei;
         const GEntry &E = a.e[ei];
         const int lu = u - E.unit_begin;
         const int rg = lu / a.n_cc;
@@ -231,17 +239,24 @@ __global__ __launch_bounds__(kThreads) void k_amax(const GroupArgs a) {
 // ---------------------------------------------------------------------------
 static inline unsigned grid_of(int64_t g) { return (unsigned)(g < 1 ? 1 : g); }
 
+// chain: the dispatch packet's barrier bit is cleared (HIP's any-order
+// launch), so the launch may start while the stream's previous launch drains.
 hipError_t launch_grouped(int fmt, int layout, bool auto_scale, const GroupArgs &a, int64_t grid,
-                          hipStream_t s) {
+                          hipStream_t s, bool chain) {
     const dim3 gd(grid_of(grid)), bd(kThreads);
+    const uint32_t fl = chain ? hipExtAnyOrderLaunch : 0;
     if (fmt == MXQ_MXFP8 && layout == MXQ_SF_LINEAR)
-        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_LINEAR, false>), gd, bd, 0, s, a);
+        hipExtLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_LINEAR, false>), gd, bd, 0, s, nullptr,
+                              nullptr, fl, a);
     else if (fmt == MXQ_MXFP8)
-        hipLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_SWIZZLED, false>), gd, bd, 0, s, a);
+        hipExtLaunchKernelGGL((k_grouped<MXQ_MXFP8, MXQ_SF_SWIZZLED, false>), gd, bd, 0, s, nullptr,
+                              nullptr, fl, a);
     else if (layout == MXQ_SF_LINEAR && !auto_scale)
-        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_LINEAR, false>), gd, bd, 0, s, a);
+        hipExtLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_LINEAR, false>), gd, bd, 0, s, nullptr,
+                              nullptr, fl, a);
     else if (!auto_scale)
-        hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_SWIZZLED, false>), gd, bd, 0, s, a);
+        hipExtLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_SWIZZLED, false>), gd, bd, 0, s, nullptr,
+                              nullptr, fl, a);
     else if (layout == MXQ_SF_LINEAR)
         hipLaunchKernelGGL((k_grouped<MXQ_NVFP4, MXQ_SF_LINEAR, true>), gd, bd, 0, s, a);
     else

@@ -28,6 +28,14 @@ __device__ __forceinline__ int xcd_grouped_unit(int b, int n) {
     return b / kBlock * kBlock + (b & 7) * G + (b >> 3) % G;
 }
 
+// Whether the XCD grouping holds for a launch of `grid` workgroups over
+// `units` units: with one workgroup per unit, workgroup b takes unit b; with
+// fewer, workgroup b takes units b, b + grid, b + 2 grid, ..., which all run
+// on XCD b % 8 when grid is a multiple of 8.
+__device__ __forceinline__ bool xcd_grouping_holds(int64_t grid, int64_t units) {
+    return grid == units || (grid & 7) == 0;
+}
+
 // The same with a group size g known only at run time (g >= 1).
 __device__ __forceinline__ int64_t xcd_grouped_unit(int64_t b, int64_t n, int g) {
     const int64_t block = (int64_t)g * 8;
@@ -62,6 +70,7 @@ struct GroupArgs {
     uint32_t *amax_bits;
     float *g_out;
     int32_t n_slots;
+    int32_t uniform_units;  // units per entry when every entry has the same count, else 0
 };
 
 constexpr int kMaxSplitsPerLaunch = 256;
@@ -139,7 +148,7 @@ struct SwizzleArgs {
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_grouped(int fmt, int layout, bool auto_scale, const GroupArgs &a, int64_t grid,
-                          hipStream_t s);
+                          hipStream_t s, bool chain = false);
 // Zero a.amax_bits[0..n_slots), then reduce each slot's amax into it.
 hipError_t launch_amax(const GroupArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,

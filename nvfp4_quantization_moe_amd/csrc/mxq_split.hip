@@ -98,7 +98,7 @@ void k_split(const SplitArgs a) {
             const int pads = a.total_units - n_row_units;
             u = u0 < pads ? n_row_units + u0 : u0 - pads;
         }
-        if ((int)gridDim.x == a.total_units && u < n_row_units)
+        if (xcd_grouping_holds(gridDim.x, a.total_units) && u < n_row_units)
             u = xcd_grouped_unit<32>(u, n_row_units);
         if (kSwz && u >= n_row_units) {
             // padding unit of split s, whose last band has fewer than 32

@@ -4,7 +4,8 @@
  * (oracle/mxq_oracle.h, test infrastructure linked only into this test).
  *
  * Covered: mx_quant_grouped (MXFP8 and NVFP4, linear and swizzled, ragged
- * rows, a strided source), nvfp4_quant_split_row_scaled (empty and ragged
+ * rows, a strided source), the same entries through mx_quant_grouped_batch
+ * (two launches, the second chained), nvfp4_quant_split_row_scaled (empty and ragged
  * experts, swizzled) and rmsnorm_quant_fused (MXFP8, swizzled).  Prints
  * "ok: N checks" and exits 0 when everything matches. */
 #include <stdint.h>
@@ -82,7 +83,7 @@ static void *hmalloc(size_t n) {
     return p;
 }
 
-static void grouped(hipStream_t s, int fmt, int layout) {
+static void grouped(hipStream_t s, int fmt, int layout, int batched) {
     enum { N = 3 };
     const int64_t cols = 768, rows[N] = {130, 1, 64}, ld[N] = {768, 1024, 768};
     const int64_t pw = fmt == MXQ_MXFP8 ? cols : cols / 2;
@@ -107,7 +108,11 @@ static void grouped(hipStream_t s, int fmt, int layout) {
         HIP_OK(hipMemcpy((void *)e[i].src, h_src[i], (size_t)(rows[i] * ld[i] * 2),
                          hipMemcpyHostToDevice));
     }
-    expect_status("mx_quant_grouped", mx_quant_grouped(fmt, layout, cols, e, N, s));
+    if (batched)
+        expect_status("mx_quant_grouped_batch",
+                      mx_quant_grouped_batch(fmt, layout, cols, e, N, 2, MXQ_CHAIN, s));
+    else
+        expect_status("mx_quant_grouped", mx_quant_grouped(fmt, layout, cols, e, N, s));
     HIP_OK(hipStreamSynchronize(s));
     for (int i = 0; i < N; ++i) {
         const int64_t sb = mxq_scale_bytes(rows[i], cols, fmt, layout);
@@ -211,7 +216,10 @@ int main(void) {
         for (int layout = 0; layout < 2; ++layout) {
             printf("grouped fmt %d layout %d\n", fmt, layout);
             fflush(stdout);
-            grouped(s, fmt, layout);
+            grouped(s, fmt, layout, 0);
+            printf("grouped batch, chained, fmt %d layout %d\n", fmt, layout);
+            fflush(stdout);
+            grouped(s, fmt, layout, 1);
         }
     printf("row-scaled split\n");
     fflush(stdout);

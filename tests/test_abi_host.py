@@ -108,6 +108,28 @@ def test_grouped_validation():
     assert _grouped(0, 1, 64, [_ent(rows=0, src=0, pay=0, sc=0)]) == OK
 
 
+def _batch(ents, per=16, flags=0, fmt=0, layout=1, cols=64):
+    arr = (_Entry * max(len(ents), 1))(*ents)
+    return mxq.lib().mx_quant_grouped_batch(fmt, layout, cols, arr, len(ents), per, flags, None)
+
+
+def test_grouped_batch_validation():
+    """Every batch of a multi-launch call is checked before the first launch:
+    a bad entry in the last batch is refused with no launch (on this machine
+    a launch could only fail, so EINVAL shows the check came first)."""
+    ents = [_ent() for _ in range(40)]
+    assert _batch([]) == EINVAL                                   # no entries
+    assert _batch(ents, per=0) == EINVAL
+    assert _batch(ents, per=17) == EINVAL
+    assert _batch(ents, flags=2) == EINVAL                        # unknown flag
+    assert _batch(ents, flags=3) == EINVAL
+    assert _batch(ents, fmt=2) == EINVAL
+    assert _batch(ents[:39] + [_ent(src=0)]) == EINVAL            # last batch
+    assert _batch(ents[:33] + [_ent(ld=60)] + ents[34:], per=5) == ESHAPE
+    assert _batch([_ent(rows=0, src=0, pay=0, sc=0)] * 20, flags=1) == OK  # no rows: no launch
+    assert mxq.lib().mx_quant_grouped_batch(0, 1, 64, None, 3, 16, 0, None) == EINVAL
+
+
 def _split(split, T=None, cols=64, src=A, g=A, pay=A, sc=A, amax=A, layout=1):
     T = sum(split) if T is None else T
     arr = (ctypes.c_int64 * max(len(split), 1))(*split)

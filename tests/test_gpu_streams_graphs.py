@@ -138,35 +138,63 @@ def test_calls_from_several_host_threads(orc):
         assert np.array_equal(u8(p), qp.ravel()) and np.array_equal(u8(s), qs)
 
 
-def test_grouped_issue_overlapped(orc):
-    """issue_overlapped alternates the launches of several calls over two
-    side streams joined to the calling stream: the bytes equal the serial
-    calls', a late producer on the calling stream is seen, and a consumer
-    queued on the calling stream after it sees every output."""
+def test_grouped_batch_chained(orc):
+    """mx_quant_grouped_batch with MXQ_CHAIN (launches after the first
+    dispatched any-order): the bytes equal the unchained call's and the
+    oracle's, a late producer on the stream is seen by every launch, and a
+    consumer queued after the call sees every output."""
     xs_cpu = workloads.small_grouped_experts(n_experts=40, rows=128, cols=512, seed=21)
     xs = [x.to(DEV) for x in xs_cpu]
-    serial = mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs)
-    halves = [mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs[:24]),
-              mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs[24:])]
-
-    def over():
-        mxq.issue_overlapped(halves)
-        return halves[0].payloads + halves[1].payloads, halves[0].scales + halves[1].scales
-    say("grouped overlap on two streams")
-    sp, ss = serial()
+    plain = mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs, max_per_launch=5)
+    chained = mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs, max_per_launch=5, chain=True)
+    say("grouped batch, chained launches")
+    sp, ss = plain()
     want = [u8(t).copy() for t in sp + ss]
     late = [x.clone() for x in xs]
     for x in xs:
         x.zero_()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        torch.cuda._sleep(20_000_000)      # the producer is late ...
-        for x, y in zip(xs, late):
-            x.copy_(y)                     # ... and restores the inputs
-        pays, scs = over()
-        copies = [t.clone() for t in pays + scs]  # a consumer on the calling stream
-    s.synchronize()
-    assert all(np.array_equal(u8(a), b) for a, b in zip(copies, want))
+        for rep in range(3):
+            for t in chained.payloads + chained.scales:
+                t.fill_(CANARY)
+            torch.cuda._sleep(20_000_000)      # the producer is late ...
+            for x, y in zip(xs, late):
+                x.copy_(y)                     # ... and restores the inputs
+            pays, scs = chained()
+            copies = [t.clone() for t in pays + scs]  # a consumer queued after the call
+            s.synchronize()
+            assert all(np.array_equal(u8(a), b) for a, b in zip(copies, want)), rep
+            for x in xs:
+                x.zero_()
     for i in (0, 17, 39):
         p, sc = orc.quantize(orc.MXFP8, orc.SWIZZLED, bf16_bits(xs_cpu[i]))
-        assert np.array_equal(u8(pays[i]), p.ravel()) and np.array_equal(u8(scs[i]), sc)
+        assert np.array_equal(want[i], p.ravel()) and np.array_equal(want[40 + i], sc)
+
+
+def test_grouped_batch_chained_graph_replay(orc):
+    """Captured into a graph, a chained batch falls back to ordinary
+    launches; each replay gives the eager bytes."""
+    xs = [x.to(DEV) for x in workloads.small_grouped_experts(n_experts=20, rows=64, cols=512,
+                                                             seed=22)]
+    gs = torch.cat([g_of(x) for x in xs])
+    call = mxq.GroupedCall(mxq.NVFP4, mxq.LINEAR, xs, global_scales=gs, max_per_launch=7,
+                           chain=True)
+    say("chained batch graph replay")
+    eager = [u8(t).copy() for t in sum(call(), [])]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            call()
+    for rep in range(3):
+        for t in call.payloads + call.scales:
+            t.fill_(CANARY)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [u8(t) for t in call.payloads + call.scales]
+        assert all(np.array_equal(a, b) for a, b in zip(eager, got)), rep
