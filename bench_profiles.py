@@ -47,8 +47,8 @@ HDR = ("Commands (`$REPO` is the repository root, `$OUT` an output folder; each 
 # --warmup + --steps layer steps.
 LAYER_LAUNCHES = 128 // 16
 KT_STEPS, PMC_STEPS = 1 + 5, 1 + 2
-# calls of one secondary workload: bench.timed's 3 warm-up calls and 5 blocks of 10
-TIMED_CALLS = 3 + 5 * 10
+# Qwen3-30B-A3B layers the kernel-trace run streams (bench.py --c2-layers default)
+C2_LAYERS = 48
 
 
 def sf_bytes(rows, C, layout):
@@ -252,13 +252,19 @@ def main(argv=None):
     # grouped launches, or 128 + 128 single-expert launches, back to back; the
     # serial grouped passes over the 48 layers come first
     rows_l, spans = [], {}
+    # bench.timed makes 3 warm-up and 5 timed passes over the 48 layers: the
+    # plain grouped passes, then the per-expert passes (first 4 layers), then
+    # the chained grouped passes (same grids as the plain ones)
+    n_pass_layers = (3 + 5) * C2_LAYERS
     for kind, per in (("grouped", 16), ("per-expert", 1)):
         grids = {p: per * (-(-r // 128) * 128 // 16) * (-(-c // 512)) * 256
                  for p, (r, c) in workloads.QWEN3_30B_A3B.items()}
         seq = [x for x in trace if "k_grouped<0, 1, false>" in x[1] and x[2] in grids.values()]
         n_call = 2 * 128 // per  # launches per layer
-        # the one-stream calls come first (the two-stream ones follow)
-        layers = [seq[i:i + n_call] for i in range(0, len(seq) - n_call + 1, n_call)][:TIMED_CALLS]
+        layers = [seq[i:i + n_call] for i in range(0, len(seq) - n_call + 1, n_call)]
+        if kind == "grouped":
+            chained = layers[n_pass_layers:2 * n_pass_layers]
+            layers = layers[:n_pass_layers]
         seq = [x for L in layers for x in L]
         kern = [sum(x[3] for x in L) for L in layers]
         span = [L[-1][5] - L[0][4] for L in layers]
@@ -267,6 +273,9 @@ def main(argv=None):
             dur = [x[3] for x in seq if x[2] == g]
             rows_l.append(f"| {kind} | {p} | {g // 256} | {len(dur)} | {avg(dur) / 1e3:,.2f} |")
     (ng, kg, sg), (ne, ke, se) = spans["grouped"], spans["per-expert"]
+    # chained launches overlap, so a layer's time is its span (first start to
+    # last end of its 16 launches)
+    sc_ = avg([L[-1][5] - L[0][4] for L in chained])
     alg30 = sum(128 * (r * c * 3 + sf_bytes(r, c // 32, 1))
                 for r, c in workloads.QWEN3_30B_A3B.values())
     write_md("k_grouped_qwen3_30b_a3b_grouped_vs_per_expert.md",
@@ -281,7 +290,13 @@ def main(argv=None):
              "| per layer | launches | kernel time us (sum) | traced span us (first start to last end) | GB/s over the span |\n"
              "|---|---|---|---|---|\n"
              f"| grouped | {ng} | {kg / 1e3:,.1f} | {sg / 1e3:,.1f} | {alg30 / sg:,.0f} |\n"
+             f"| grouped, chained (MXQ_CHAIN) | {ng} | launches overlap | {sc_ / 1e3:,.1f} | "
+             f"{alg30 / sc_:,.0f} |\n"
              f"| per-expert | {ne} | {ke / 1e3:,.1f} | {se / 1e3:,.1f} | {alg30 / se:,.0f} |\n\n"
+             "Chained: mx_quant_grouped_batch with MXQ_CHAIN, the 7 launches after the first of "
+             "each call dispatched any-order; a layer's time is the span of its 16 launches.  "
+             f"Mean over the {len(chained)} chained layer passes; plain grouped over "
+             f"{n_pass_layers}.\n\n"
              f"Each launch beyond the 16 grouped ones costs {(ke - kg) / (ne - ng) / 1e3:.2f} us of "
              "kernel time: the fixed ramp and tail of a launch, which grouping pays once per 16 "
              "experts.  Kernel tracing adds its own host-side cost to every launch, so the traced "

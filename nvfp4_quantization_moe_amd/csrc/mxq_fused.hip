@@ -61,13 +61,28 @@ void k_fused(const FusedArgs a) {
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     bool staged = false;  // gamma is in LDS (uniform)
     for (int lu0 = blockIdx.x; lu0 < a.total_units; lu0 += gridDim.x) {
-        // the 8 rows whose swizzled codes share 16-byte lines on one XCD
-        const int lu = LAYOUT == MXQ_SF_SWIZZLED && xcd_grouping_holds(gridDim.x, a.total_units)
-                           ? xcd_grouped_unit<8 / RPU>(lu0, a.total_units)
-                           : lu0;
-        const int r = lu * RPU + q;
+        int lu = lu0;
+        int r;
+        if (LAYOUT == MXQ_SF_SWIZZLED && RPU == 1) {
+            // one-row units, a 128-row band's 128 units in the order of its
+            // scale lines: the 16 units of each XCD group are the rows whose
+            // codes fill 4 whole 16-byte lines (64 contiguous bytes of every
+            // tile), rows p + 32 q for 4 consecutive p and q = 0..3, so one
+            // L2 writes them whole
+            if (xcd_grouping_holds(gridDim.x, a.total_units))
+                lu = xcd_grouped_unit<16>(lu0, a.total_units);
+            const int i = lu & 127, k = i >> 5, j = i & 31;
+            r = (lu & ~127) + 8 * k + (j >> 2) + 32 * (j & 3);
+        } else {
+            // four-row units: the 8 consecutive rows whose codes share
+            // 128-byte lines on one XCD
+            if (LAYOUT == MXQ_SF_SWIZZLED && xcd_grouping_holds(gridDim.x, a.total_units))
+                lu = xcd_grouped_unit<8 / RPU>(lu0, a.total_units);
+            r = lu * RPU + q;
+        }
         const bool live = r < a.T;
-        const bool unit_live = lu * RPU < a.T;  // uniform: any live row in the unit
+        const int r0 = RPU == 1 ? r : lu * RPU;  // the unit's first row
+        const bool unit_live = r0 < a.T;  // uniform: any live row in the unit
         const bool stage_now = !staged && unit_live;
         const int64_t rb = (int64_t)r * H;
         u32x4 xv[NCHW];
@@ -142,7 +157,6 @@ void k_fused(const FusedArgs a) {
             for (int c = lane; c < a.sf_stride; c += kWave) stage[q * a.sf_stride + c] = 0;
         }
         __syncthreads();
-        const int r0 = lu * RPU;
         if constexpr (LAYOUT == MXQ_SF_SWIZZLED) {
             // row r0 + j's 4 codes of tile t: one 4-byte slot per tile
             const int tiles = a.sf_stride >> 2;
