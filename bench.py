@@ -372,7 +372,7 @@ def main():
         t2 = (time.perf_counter() - t0) / args.steps
         out["step_two_streams"] = {"ms_per_step": round(t2 * 1e3, 4),
                                    "GBps": round(step_bytes / t2 / 1e9, 1)}
-        out["other_workloads"] = extra_workloads(torch, mxq, workloads, dev, args.c2_layers)
+        out["other_workloads"] = extra_workloads(torch, mxq, workloads, dev, args.c2_layers, side)
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (the oracle)")
         out["cpu_baseline"] = cpu_baseline(torch, layers[0]["gate_up"], gsc[0]["gate_up"],
@@ -397,7 +397,7 @@ def timed(torch, fn, iters, warm=3, reps=5):
     return sorted(per)[len(per) // 2]
 
 
-def extra_workloads(torch, mxq, workloads, dev, n_layers=48):
+def extra_workloads(torch, mxq, workloads, dev, n_layers=48, side=None):
     import ctypes
     res = {}
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
@@ -441,6 +441,17 @@ def extra_workloads(torch, mxq, workloads, dev, n_layers=48):
     # the same calls with MXQ_CHAIN: within each call, launches after the
     # first are dispatched any-order and start while the previous one drains
     t2 = timed(torch, lambda i: [c() for c in chained], 1) / n_layers
+    # the same calls over two side streams (default priority), launch j of
+    # each call on stream j % 2, joined back once per pass over the layers or
+    # once per layer; each output slice is written from one stream.  The
+    # side streams are the ones the two-stream step used: a process gets 4
+    # hardware queues (HIP's default), and streams beyond them share one,
+    # which serializes them (measured 359 instead of 289 us per layer)
+    if side is None:
+        side = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    tw = timed(torch, lambda i: mxq.issue_interleaved(grouped, side), 1) / n_layers
+    tl = timed(torch, lambda i: [mxq.issue_interleaved(grouped[2 * l:2 * l + 2], side)
+                                 for l in range(n_layers)], 1) / n_layers
     per_launch = len(single[0]) - 2 * E // G
     res["qwen3_30b_a3b_48_layers_mxfp8_swizzled"] = {
         "layers": n_layers, "alg_bytes_per_layer": nbytes,
@@ -448,6 +459,9 @@ def extra_workloads(torch, mxq, workloads, dev, n_layers=48):
         "grouped_GBps": round(nbytes / tg / 1e9, 1),
         "grouped_chained_us_per_layer": round(t2 * 1e6, 1),
         "chained_GBps": round(nbytes / t2 / 1e9, 1),
+        "two_streams_one_join_us_per_layer": round(tw * 1e6, 1),
+        "two_streams_one_join_GBps": round(nbytes / tw / 1e9, 1),
+        "two_streams_join_per_layer_us_per_layer": round(tl * 1e6, 1),
         "per_expert_256_launches_us_per_layer": round(ts * 1e6, 1),
         "per_expert_GBps": round(nbytes / ts / 1e9, 1),
         "overhead_per_extra_launch_us": round((ts - tg) / per_launch * 1e6, 2)}

@@ -254,7 +254,9 @@ def main(argv=None):
     rows_l, spans = [], {}
     # bench.timed makes 3 warm-up and 5 timed passes over the 48 layers: the
     # plain grouped passes, then the per-expert passes (first 4 layers), then
-    # the chained grouped passes (same grids as the plain ones)
+    # the chained grouped passes, the two-stream passes joined once per pass
+    # and those joined once per layer (same grids as the plain ones; the
+    # trace lists dispatches in issue order)
     n_pass_layers = (3 + 5) * C2_LAYERS
     for kind, per in (("grouped", 16), ("per-expert", 1)):
         grids = {p: per * (-(-r // 128) * 128 // 16) * (-(-c // 512)) * 256
@@ -264,6 +266,8 @@ def main(argv=None):
         layers = [seq[i:i + n_call] for i in range(0, len(seq) - n_call + 1, n_call)]
         if kind == "grouped":
             chained = layers[n_pass_layers:2 * n_pass_layers]
+            two_once = layers[2 * n_pass_layers:3 * n_pass_layers]
+            two_layer = layers[3 * n_pass_layers:4 * n_pass_layers]
             layers = layers[:n_pass_layers]
         seq = [x for L in layers for x in L]
         kern = [sum(x[3] for x in L) for L in layers]
@@ -276,6 +280,14 @@ def main(argv=None):
     # chained launches overlap, so a layer's time is its span (first start to
     # last end of its 16 launches)
     sc_ = avg([L[-1][5] - L[0][4] for L in chained])
+
+    # launches on two streams overlap: a pass's time is its first start to its
+    # last end, over its 48 layers; a layer joined on its own, its own span
+    def span_of(Ls):
+        return max(x[5] for L in Ls for x in L) - min(x[4] for L in Ls for x in L)
+    passes = [two_once[i:i + C2_LAYERS] for i in range(0, len(two_once), C2_LAYERS)]
+    s2o = avg([span_of(P) / len(P) for P in passes])
+    s2l = avg([span_of([L]) for L in two_layer])
     alg30 = sum(128 * (r * c * 3 + sf_bytes(r, c // 32, 1))
                 for r, c in workloads.QWEN3_30B_A3B.values())
     write_md("k_grouped_qwen3_30b_a3b_grouped_vs_per_expert.md",
@@ -292,11 +304,18 @@ def main(argv=None):
              f"| grouped | {ng} | {kg / 1e3:,.1f} | {sg / 1e3:,.1f} | {alg30 / sg:,.0f} |\n"
              f"| grouped, chained (MXQ_CHAIN) | {ng} | launches overlap | {sc_ / 1e3:,.1f} | "
              f"{alg30 / sc_:,.0f} |\n"
+             f"| grouped, two streams, one join per {C2_LAYERS} layers | {ng} | launches overlap | "
+             f"{s2o / 1e3:,.1f} | {alg30 / s2o:,.0f} |\n"
+             f"| grouped, two streams, one join per layer | {ng} | launches overlap | "
+             f"{s2l / 1e3:,.1f} | {alg30 / s2l:,.0f} |\n"
              f"| per-expert | {ne} | {ke / 1e3:,.1f} | {se / 1e3:,.1f} | {alg30 / se:,.0f} |\n\n"
              "Chained: mx_quant_grouped_batch with MXQ_CHAIN, the 7 launches after the first of "
              "each call dispatched any-order; a layer's time is the span of its 16 launches.  "
              f"Mean over the {len(chained)} chained layer passes; plain grouped over "
-             f"{n_pass_layers}.\n\n"
+             f"{n_pass_layers}.  Two streams: issue_interleaved, launch j of each call on side "
+             "stream j % 2, the streams joined back to the caller's once per pass over the "
+             f"{C2_LAYERS} layers (the pass's span over {C2_LAYERS}; mean of {len(passes)} passes) "
+             f"or once per layer (the layer's span; mean of {len(two_layer)}).\n\n"
              f"Each launch beyond the 16 grouped ones costs {(ke - kg) / (ne - ng) / 1e3:.2f} us of "
              "kernel time: the fixed ramp and tail of a launch, which grouping pays once per 16 "
              "experts.  Kernel tracing adds its own host-side cost to every launch, so the traced "

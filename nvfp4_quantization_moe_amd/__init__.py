@@ -19,7 +19,7 @@ __all__ = [
     "MXFP8", "NVFP4", "LINEAR", "SWIZZLED", "MAX_GROUP", "SPLIT_MODES", "MxqError",
     "mx_quant_grouped", "nvfp4_quant_grouped_auto", "nvfp4_quant_split",
     "nvfp4_quant_split_row_scaled", "mxfp8_quant_split", "rmsnorm_quant_fused", "scale_swizzle",
-    "GroupedCall", "GroupedAutoCall", "SplitCall", "FusedCall", "CHAIN",
+    "GroupedCall", "GroupedAutoCall", "SplitCall", "FusedCall", "CHAIN", "issue_interleaved",
     "scale_bytes", "split_scale_offset", "set_max_workgroups", "library_path", "lib",
 ]
 
@@ -196,6 +196,58 @@ class GroupedCall:
                                             len(self.srcs), self.per, self.flags, stream),
                "mx_quant_grouped_batch")
         return self.payloads, self.scales
+
+    def issue(self, streams):
+        """Issue launch j of this call (entries j*per .. j*per + per - 1) on
+        streams[j % len(streams)], with no ordering against any other work:
+        issue_interleaved orders the streams.  A launch position always goes
+        to the same stream, so calls that reuse one set of outputs write each
+        output from one stream."""
+        n = len(self.srcs)
+        size = ctypes.sizeof(_Entry)
+        for j, b in enumerate(range(0, n, self.per)):
+            ents = ctypes.cast(ctypes.byref(self._ents, b * size), ctypes.POINTER(_Entry))
+            s = ctypes.c_void_p(streams[j % len(streams)].cuda_stream)
+            _check(lib().mx_quant_grouped_batch(self.fmt, self.layout, self.cols, ents,
+                                                min(self.per, n - b), self.per, 0, s),
+                   "mx_quant_grouped_batch")
+        return self.payloads, self.scales
+
+
+def issue_interleaved(calls, streams):
+    """Issue the launches of several GroupedCall objects over side streams.
+
+    The streams (torch streams of the calls' device, default priority: work
+    on streams of other priorities can starve) first wait for the work queued
+    on the current stream; each call's launch j then goes to streams[j %
+    len(streams)] (GroupedCall.issue); finally the current stream waits for
+    every stream.  Launches on different streams may run at the same time,
+    so no output may be written by two launches that land on different
+    streams (calls that reuse one set of outputs with the same launch layout
+    are safe: each output slice stays on one stream).  A process gets a few
+    hardware queues (4 by default in HIP); streams beyond them share one and
+    run one after another, so reuse a few side streams.  Two streams took a
+    Qwen3-30B-A3B layer's 16 launches from 345 to 295 us per layer when the
+    join covered 8 layers, 325 us when it covered one; launches of 300 MB and
+    more gain about 1 %."""
+    calls = list(calls)
+    streams = list(streams)
+    if not calls or not streams:
+        raise ValueError("issue_interleaved needs at least one call and one stream")
+    dev = calls[0].device
+    for s in streams:
+        if s.device != dev or s.priority != 0:
+            raise ValueError("streams must be default-priority streams of the calls' device")
+    for c in calls:
+        if not isinstance(c, GroupedCall) or c.device != dev:
+            raise ValueError("calls must be GroupedCall objects on one device")
+    cur = torch.cuda.current_stream(dev)
+    for s in streams:
+        s.wait_stream(cur)
+    for c in calls:
+        c.issue(streams)
+    for s in streams:
+        cur.wait_stream(s)
 
 
 class GroupedAutoCall:

@@ -20,8 +20,12 @@
 // persistent grid with software-pipelined loads.
 //
 // Unit u runs on workgroup u, in plain dispatch order, except that with
-// linear scales every 8 consecutive units run on one XCD (1-3 % faster; no
-// gain swizzled, whose units write whole scale segments); the units in flight
+// linear scales every 8 consecutive units run on one XCD (1-3 % faster).
+// Swizzled, the same grouping made the Qwen3-235B gate_up launches 2 % slower,
+// and on rows of 1.5 chunks (768 columns), where the plain order puts every
+// full chunk on an even XCD and every half chunk on an odd one, evening out
+// the XCDs left the launch time unchanged: the launch is bound by HBM, not by
+// the busiest XCD.  The units in flight
 // cover one contiguous stretch of every tensor (measured faster than giving
 // each XCD a contiguous range).  The quantize kernel uses no global atomics, no scratch
 // and no inter-workgroup ordering: every byte has one writer, and the bytes

@@ -198,3 +198,38 @@ def test_grouped_batch_chained_graph_replay(orc):
         torch.cuda.synchronize()
         got = [u8(t) for t in call.payloads + call.scales]
         assert all(np.array_equal(a, b) for a, b in zip(eager, got)), rep
+
+
+def test_grouped_issue_interleaved(orc):
+    """issue_interleaved over two side streams: every launch sees a late
+    producer on the current stream, a consumer queued after it sees every
+    output, and the bytes equal the serial calls' and the oracle's.  The
+    calls share one set of outputs, as a benchmark's layers do."""
+    xs_cpu = [workloads.small_grouped_experts(n_experts=40, rows=128, cols=512, seed=31 + k)
+              for k in range(3)]
+    xs = [[x.to(DEV) for x in layer] for layer in xs_cpu]
+    first = mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs[0], max_per_launch=5)
+    calls = [first] + [mxq.GroupedCall(mxq.MXFP8, mxq.SWIZZLED, xs[k], first.payloads,
+                                       first.scales, max_per_launch=5) for k in (1, 2)]
+    say("grouped calls interleaved over two streams")
+    calls[2]()  # the last call's bytes are what the shared outputs end with
+    want = [u8(t).copy() for t in first.payloads + first.scales]
+    late = [x.clone() for x in xs[2]]
+    side = [torch.cuda.Stream(), torch.cuda.Stream()]
+    with pytest.raises(ValueError):
+        mxq.issue_interleaved(calls, [])
+    for rep in range(3):
+        for t in first.payloads + first.scales:
+            t.fill_(CANARY)
+        for x in xs[2]:
+            x.zero_()
+        torch.cuda._sleep(20_000_000)      # the producer is late ...
+        for x, y in zip(xs[2], late):
+            x.copy_(y)                     # ... and restores the last call's inputs
+        mxq.issue_interleaved(calls, side)
+        copies = [t.clone() for t in first.payloads + first.scales]  # a consumer after it
+        torch.cuda.current_stream().synchronize()
+        assert all(np.array_equal(u8(a), b) for a, b in zip(copies, want)), rep
+    for i in (0, 13, 39):
+        p, sc = orc.quantize(orc.MXFP8, orc.SWIZZLED, bf16_bits(xs_cpu[2][i]))
+        assert np.array_equal(want[i], p.ravel()) and np.array_equal(want[40 + i], sc)
