@@ -384,17 +384,21 @@ def main(argv=None):
         fmt = int(f)
         by_grid = collections.defaultdict(list)
         for Tt in (1, 16, 64, 256, 1024, 4096):
+            if Tt == 1 or 16 < Tt < 32:
+                # k_fused_tiny: one 1024-thread workgroup per live row
+                by_grid[("k_fused_tiny<" + f + ">", Tt * 1024)].append(Tt)
+                continue
             # swizzled units cover the padding rows: sixteen waves per row up to
             # T = 512, four up to 1536, else two waves and four rows per unit
             rt = -(-Tt // 128) * 128
             grid = rt * 1024 if Tt <= 512 else rt * 256 if Tt <= 1536 else rt // 4 * 512
-            by_grid[grid].append(Tt)
-        for grid, Ts in by_grid.items():
+            by_grid[(f"k_fused<{f}, 1,", grid)].append(Tt)
+        for (kname, grid), Ts in by_grid.items():
             for k, Tt in enumerate(Ts):
                 pw = H if fmt == 0 else H // 2
                 nsc = sf_bytes(Tt, H // (32 if fmt == 0 else 16), 1)
                 alg = Tt * H * 8 + Tt * pw + nsc + 2 * H + (4 if fmt else 0)
-                m = lambda n, g, f=f, grid=grid: f"k_fused<{f}, 1," in n and g == grid
+                m = lambda n, g, kname=kname, grid=grid: kname in n and g == grid
 
                 def nth(rows, k=k, nT=len(Ts)):  # T values sharing a grid run in order
                     per = len(rows) // nT
@@ -411,12 +415,16 @@ def main(argv=None):
     write_md("k_fused_rmsnorm_h7168.md",
              "k_fused -- residual add + RMSNorm + quantize, H = 7168, swizzled scales, MI355X",
              "Algorithmic bytes: x, residual in (4 B/elem), residual_out, norm_out (4 B/elem), "
-             "payload, padded scales, gamma.  T <= 512 runs sixteen waves per row (1024-thread "
-             "workgroups), T = 1024 four (256 threads), one row per workgroup (the padding rows "
-             "of a swizzled 128-row tile are workgroups of their own); T = 4096 runs two waves "
-             "per row, four rows per 512-thread workgroup.  T = 1, 16 and 64 share one grid "
-             "(128 workgroups), as do T = 256 and 1024; their dispatches are told apart by "
-             "order.\n\n" + calib + "\n"
+             "payload, padded scales, gamma.  T = 1 runs k_fused_tiny: one 1024-thread "
+             "workgroup for the live row, which also writes the padding rows' zero scales.  "
+             "Otherwise T <= 512 runs sixteen waves per row (1024-thread workgroups), T = 1024 "
+             "four (256 threads), one row per workgroup (the padding rows of a swizzled 128-row "
+             "tile are workgroups of their own); T = 4096 runs two waves per row, four rows per "
+             "512-thread workgroup.  T = 16 and 64 share one grid (128 workgroups), as do "
+             "T = 256 and 1024; their dispatches are told apart by order.  bench.py times each "
+             "T as replays of a captured graph of 8 calls (a decode step runs the epilogue "
+             "inside a graph; called one at a time from Python, the host's cost per call "
+             "exceeds the kernel's and the GPU idles between launches).\n\n" + calib + "\n"
              "| format | T | n | avg us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
              "|---|---|---|---|---|---|---|---|---|\n" + "\n".join(rows_f) + "\n")
 

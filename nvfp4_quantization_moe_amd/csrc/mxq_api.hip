@@ -352,9 +352,18 @@ int rmsnorm_quant_fused(int fmt, int layout, const void *x, const void *residual
         layout == MXQ_SF_SWIZZLED ? kFusedWideMaxTSwizzled : kFusedWideMaxTLinear;
     a.wpr = T <= wide_max ? 16 : T <= kFusedFourWaveMaxT ? 4 : 2;
     a.rpu = a.wpr == 2 ? 4 : 1;
-    const int64_t units = row_groups(T, layout, a.rpu);
-    a.total_units = (int32_t)units;
-    hipError_t err = launch_fused(fmt, layout, a, grid_for(units), (hipStream_t)stream);
+    hipError_t err;
+    if (layout == MXQ_SF_SWIZZLED && fused_tiny_rows(T) && H <= 16 * kChunk &&
+        grid_for(T) == T) {
+        // a few rows: one workgroup per live row, no padding units
+        a.wpr = 16;
+        a.total_units = (int32_t)T;
+        err = launch_fused_tiny(fmt, a, (hipStream_t)stream);
+    } else {
+        const int64_t units = row_groups(T, layout, a.rpu);
+        a.total_units = (int32_t)units;
+        err = launch_fused(fmt, layout, a, grid_for(units), (hipStream_t)stream);
+    }
     return err == hipSuccess ? MXQ_OK : MXQ_ELAUNCH;
 }
 

@@ -177,6 +177,104 @@ void k_fused(const FusedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// A few rows, swizzled scales: one 1024-thread workgroup per live row (fewer
+// than 32 rows, H up to 16 x 512), sixteen waves of one 512-column step each,
+// and no units for the padding rows.  Each row is the only live row of its
+// 16-byte scale line (line p = the row), so it writes its 4 codes of a tile
+// with the zeros of the line's three padding slots in one store; the lines
+// T..31 of every tile, which hold no live row, are zeroed by the same
+// workgroups.  Only the XCDs that run a live row then fetch the code and
+// gamma: at T = 1 one XCD instead of eight, FETCH + WRITE 1.07x the
+// algorithmic bytes instead of 1.44-1.57x, in the same time.  A kernel of its
+// own: the general kernel's code is larger, and at a few rows a launch costs
+// little more than its instruction fetch and memory latency (the general
+// kernel with this logic added ran 0.3 us slower at T = 1).  The arithmetic
+// and the sum order are the general kernel's with sixteen waves per row.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ __launch_bounds__(kFusedTinyThreads) void k_fused_tiny(const FusedArgs a) {
+    using Tr = FmtTraits<FMT>;
+    constexpr int kWaves = kFusedTinyThreads / kWave;
+    constexpr int kLanesPerTile = 4 * Tr::kLanesPerBlock;  // 4 blocks of codes per tile
+    __shared__ float red[kWaves];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int r = blockIdx.x;
+    const int H = a.H;
+    const int col = w * kChunk + lane * 8;
+    const bool has = col < H;
+    const int64_t rb = (int64_t)r * H;
+    const float g = FMT == MXQ_NVFP4 ? *a.g : 0.0f;
+    const NvG G = nv_prepare(g);
+    u32x4 xv = u32x4{0, 0, 0, 0}, rv = u32x4{0, 0, 0, 0}, gm = u32x4{0, 0, 0, 0};
+    if (has) {
+        xv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + rb + col));
+        rv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.res + rb + col));
+        gm = *reinterpret_cast<const u32x4 *>(a.gamma + col);
+    }
+    // lines T..31 of every tile hold no live row: zeroed here, between the
+    // row's loads and their first use.  One counter tracks a wave's loads and
+    // stores, so the wave waits for these stores with its loads, under whose
+    // latency they complete; issued after the row (measured 0.1-0.2 us
+    // slower) they would lengthen the launch's tail.
+    const int tiles = a.sf_stride >> 2;
+    const int ne = 32 - a.T;
+    for (int k = r * kFusedTinyThreads + (int)threadIdx.x; k < tiles * ne;
+         k += a.T * kFusedTinyThreads) {
+        const int t = k / ne, p = a.T + k - t * ne;
+        *reinterpret_cast<u32x4 *>(a.scales + (int64_t)t * 512 + p * 16) = u32x4{0, 0, 0, 0};
+    }
+    float acc = 0.0f;
+    if (has) {
+        u32x4 sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t blo = f32_to_bf16(bf16_lo(xv[j]) + bf16_lo(rv[j]));
+            const uint32_t bhi = f32_to_bf16(bf16_hi(xv[j]) + bf16_hi(rv[j]));
+            const float flo = __uint_as_float(blo << 16);
+            const float fhi = __uint_as_float(bhi << 16);
+            acc = __builtin_fmaf(flo, flo, acc);
+            acc = __builtin_fmaf(fhi, fhi, acc);
+            sum[j] = blo | (bhi << 16);
+        }
+        xv = sum;  // the bf16 residual sum
+        __builtin_nontemporal_store(sum, reinterpret_cast<u32x4 *>(a.res_out + rb + col));
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) red[w] = acc;
+    __syncthreads();
+    float ss = red[0];
+#pragma unroll
+    for (int p = 1; p < kWaves; ++p) ss += red[p];
+    const float inv = 1.0f / __builtin_sqrtf(ss / (float)H + a.eps);
+    u32x4 nv = u32x4{0, 0, 0, 0};
+    if (has) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float nlo = (bf16_lo(xv[j]) * bf16_lo(gm[j])) * inv;
+            const float nhi = (bf16_hi(xv[j]) * bf16_hi(gm[j])) * inv;
+            nv[j] = pack_bf16(nlo, nhi);
+        }
+        __builtin_nontemporal_store(nv, reinterpret_cast<u32x4 *>(a.norm_out + rb + col));
+    }
+    u32x2 pay;
+    const uint32_t code = quant8<FMT>(nv, G, pay);  // whole wave
+    const int64_t payload_ld = FMT == MXQ_MXFP8 ? H : H / 2;
+    if (has) store_payload<FMT>(a.payload + (int64_t)r * payload_ld, col, pay);
+    // a tile's 4 codes come from the first lanes of its 4 blocks; its first
+    // lane writes them with the line's zero slots (a tile lies wholly inside
+    // or outside the row: C is a multiple of 4)
+    const uint32_t c1 = __shfl(code, lane + Tr::kLanesPerBlock);
+    const uint32_t c2 = __shfl(code, lane + 2 * Tr::kLanesPerBlock);
+    const uint32_t c3 = __shfl(code, lane + 3 * Tr::kLanesPerBlock);
+    if (has && lane % kLanesPerTile == 0) {
+        const int t = (w * kChunk + lane * 8) / (4 * Tr::kBlock);
+        *reinterpret_cast<u32x4 *>(a.scales + (int64_t)t * 512 + r * 16) =
+            u32x4{code | (c1 << 8) | (c2 << 16) | (c3 << 24), 0, 0, 0};
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Linear -> swizzled scale layout.  A unit is one 128-row band by up to
 // kSwizzleTiles tiles (4 scale columns each): its linear codes are read row
 // by row into LDS, then its tiles leave as one contiguous run of 16-byte
@@ -292,6 +390,15 @@ hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, h
         fused_wpr<MXQ_NVFP4, MXQ_SF_LINEAR>(a, gd, lds, s);
     else
         fused_wpr<MXQ_NVFP4, MXQ_SF_SWIZZLED>(a, gd, lds, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_tiny(int fmt, const FusedArgs &a, hipStream_t s) {
+    const dim3 gd(grid_of(a.T)), bd(kFusedTinyThreads);
+    if (fmt == MXQ_MXFP8)
+        hipLaunchKernelGGL(k_fused_tiny<MXQ_MXFP8>, gd, bd, 0, s, a);
+    else
+        hipLaunchKernelGGL(k_fused_tiny<MXQ_NVFP4>, gd, bd, 0, s, a);
     return hipGetLastError();
 }
 

@@ -127,6 +127,21 @@ struct FusedArgs {
 //  * beyond, two waves per row and four-row units (bandwidth bound).  The
 //    last two tie near T = 1536; at T = 2048 four-row units are 1-4 us faster.
 constexpr int64_t kFusedWideMaxTSwizzled = 512;
+// Swizzled, H up to 16 x 512: k_fused_tiny (one workgroup per live row, no
+// padding units) at T = 1 and at 17..31 rows; the general kernel from 2 to 16
+// rows, where its scale-line unit order puts 4 live rows on each of up to 4
+// XCDs (whole 64-byte line segments, gamma fetched by 4 L2s).  Measured at
+// H = 7168, MXFP8, kernel trace (this kernel / the general one):
+//   T = 1: 3.44 / 3.44 us, 1.07 / 1.44x the algorithmic bytes;
+//   T = 2..16: 0.04-0.16 us slower, 1.16-1.29x / 1.08-1.27x;
+//   T = 24, 31: 4.16 / 4.64 us.
+// Below 32 rows every row is the only live row of its scale line.
+constexpr int64_t kFusedTinyMaxT = 31;
+static_assert(kFusedTinyMaxT < 32, "k_fused_tiny writes each row as the only live row of its line");
+__host__ __device__ constexpr bool fused_tiny_rows(int64_t T) {
+    return T == 1 || (T > 16 && T <= kFusedTinyMaxT);
+}
+constexpr int kFusedTinyThreads = 1024;
 constexpr int64_t kFusedWideMaxTLinear = 256;
 constexpr int64_t kFusedFourWaveMaxT = 1536;
 
@@ -154,6 +169,7 @@ hipError_t launch_amax(const GroupArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a, int64_t grid,
                         hipStream_t s);
 hipError_t launch_fused(int fmt, int layout, const FusedArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_fused_tiny(int fmt, const FusedArgs &a, hipStream_t s);
 hipError_t launch_swizzle(const SwizzleArgs &a, int64_t grid, hipStream_t s);
 
 // Largest supported row lengths.  Grouped units take 512-column chunks, so

@@ -252,6 +252,28 @@ def test_fused_widths_both_row_splits(orc, fmt, layout):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+def test_fused_swizzled_partial_bands(orc, fmt):
+    """Swizzled one-row units are the live rows only: the live rows of a
+    partial last band write its padding (a line's last live row carries the
+    zeros of the slots after it; lines with no live row are zeroed by the
+    band's units).  Every count of live rows around the line and band
+    boundaries, both launch shapes of one-row units (sixteen waves up to
+    T = 512, four above), and capped grids; every byte of the canary-filled
+    scales against the oracle."""
+    for T in (1, 2, 3, 17, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 159, 160,
+              161, 255, 256, 257, 300, 511, 512, 513, 600, 1023, 1025):
+        say("fused partial band, fmt", fmt, "T", T)
+        _fused_check(orc, T, 256, fmt, mxq.SWIZZLED, seed=900 + T)
+    try:
+        for T, cap in ((1, 1), (5, 2), (40, 3), (200, 7), (700, 8)):
+            mxq.set_max_workgroups(cap)
+            say("fused partial band, grid cap", cap, "T", T)
+            _fused_check(orc, T, 256, fmt, mxq.SWIZZLED, seed=950 + T)
+    finally:
+        mxq.set_max_workgroups(0)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_fused_grid_invariance(orc, fmt):
     try:
         for T in (100, 2100):
