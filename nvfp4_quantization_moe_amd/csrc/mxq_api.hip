@@ -273,7 +273,8 @@ int quant_split(int fmt, bool row_scaled, const void *src, int64_t total_rows, i
         a.row_off[n] = (int32_t)rows;
         a.unit_off[n] = (int32_t)pads;
         a.band_off[n] = (int32_t)bands;
-        const int64_t units = (rows + kSplitUnitRows - 1) / kSplitUnitRows + pads;
+        const int64_t ur = split_unit_rows(layout);
+        const int64_t units = (rows + ur - 1) / ur + pads;
         a.total_units = (int32_t)units;
         if (units > 0) {
             hipError_t err =

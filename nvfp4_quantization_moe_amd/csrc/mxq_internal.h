@@ -14,7 +14,7 @@ constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kRowsPerWave = 4;                // rows per wave in a grouped unit
 constexpr int kUnitRows = 4 * kRowsPerWave;   // rows per grouped work unit
 constexpr int kChunk = 512;    // row elements per wave step (8 per lane)
-constexpr int kSplitThreads = 256;  // split workgroup: 4 waves, 2 per row
+constexpr int kSplitThreads = 256;  // split workgroup: 4 waves
 
 // Workgroup b of a launch runs on XCD b % 8, and each XCD has its own L2.
 // Within every block of 8*G workgroups, XCD x takes units G*x .. G*x + G-1 of
@@ -74,7 +74,12 @@ struct GroupArgs {
 };
 
 constexpr int kMaxSplitsPerLaunch = 256;
-constexpr int kSplitUnitRows = 2;     // rows per split work unit
+// Waves per row and rows per split work unit (the workgroup's 4 waves):
+// swizzled, two rows of two waves (the rows' 4-byte scale slots share
+// 16-byte lines, so a store of both rows' slots coalesces); linear, one row
+// of four waves (shorter chains of loads per wave).
+constexpr int split_wpr(int layout) { return layout == MXQ_SF_SWIZZLED ? 2 : 4; }
+constexpr int split_unit_rows(int layout) { return kSplitThreads / 64 / split_wpr(layout); }
 
 // Up to 256 consecutive non-empty splits of a concatenated activation (the
 // host leaves empty splits out: they own no rows and no scale bytes).  Work units
@@ -181,10 +186,10 @@ constexpr int64_t kMaxColsNv = 16384;
 constexpr int64_t kMaxSplitCols = 16384;
 constexpr int64_t kMaxFusedH = 16384;
 
-// Whole-row kernels (split, fused) keep half a row per wave in registers:
-// this many 512-column steps per wave.
-inline int half_row_steps(int64_t cols) {
-    const int64_t n = ((cols + kChunk - 1) / kChunk + 1) / 2;
+// The split keeps 1/wpr of a row per wave in registers: this many 512-column
+// steps per wave, rounded up to an instantiated count.
+inline int split_steps(int64_t cols, int wpr) {
+    const int64_t n = ((cols + kChunk - 1) / kChunk + wpr - 1) / wpr;
     if (n <= 1) return 1;
     if (n <= 2) return 2;
     if (n <= 4) return 4;

@@ -5,12 +5,18 @@
 // scale, row-scaled NVFP4 (each row under an encode scale derived from its own
 // amax) and MXFP8.
 //
-// A work unit is 2 consecutive rows of the activation, whatever experts they
-// belong to, taken by a workgroup of 4 waves, two per row.  Consecutive rows
+// A work unit is consecutive rows of the activation, whatever experts they
+// belong to, taken by a workgroup of 4 waves: with swizzled scales 2 rows of
+// two waves each, with linear scales 1 row of four waves.  Consecutive rows
 // are one contiguous stretch of memory, which HBM serves best, and many small
 // workgroups keep the most loads in flight.  Linear scales of the whole
 // activation are one [rows, C] matrix, so the unit's codes leave as one
-// contiguous run.  With swizzled scales each row's code for tile t is a
+// contiguous run; one row of four waves (4 steps of 512 columns per wave at
+// 7168 columns, 7 waves per SIMD) ran the routed NVFP4 split in 27.3-27.6 us
+// against 29.5-30.1 with two rows of two waves.  Swizzled, the same shape ran
+// 0.5-1.5 us slower: one row's 4-byte scale slots lie 512 bytes apart, while
+// the slots of two adjacent rows share 16-byte lines, so each store of a
+// two-row unit covers both.  With swizzled scales each row's code for tile t is a
 // 4-byte slot at its expert's region, band, 16-byte line p = local row % 32
 // and slot q = local row / 32 % 4.  The last live row of a line also writes
 // the zeros of the padding slots after it, in the same store (16 bytes for a
@@ -27,6 +33,7 @@
 //   same, linear codes of partial bands reordered by a 2nd kernel     39-41 / 39-41
 //   4 consecutive rows (512 or 256 threads)                           33-34.6 / 29.4-31
 //   2 consecutive rows (256 threads)                                  33.3-34.4 / 29.1
+//   (2 rows of four waves, 512 threads, 6-8 waves per SIMD: 35.8-37.7)
 //   same, 4 consecutive units on one XCD                              32.1-32.3 / 29.3
 //   same, padding units dispatched first                              30.8-31.2 / 28.7-28.9
 //   same, 8, 16 or 64 units per XCD                                   30.0-30.8 / 28.8-30.1
@@ -48,29 +55,35 @@
 
 namespace mxq {
 
-// Register budgets without spills: up to 7 half-row steps in 96 VGPRs (5
-// waves per SIMD) with one encode scale, in 128 (4) row-scaled; 8 steps in
-// 128 or, row-scaled, 168 (3); wider rows get the whole register file.
-constexpr int split_waves(int nch2, bool rowsc) {
-    return nch2 <= 7 ? (rowsc ? 4 : 5) : nch2 == 8 ? (rowsc ? 3 : 4) : 1;
+// Register budgets without spills: up to 4 steps per wave in 72 VGPRs (7
+// waves per SIMD) with one encode scale, in 84 (6) row-scaled, when four waves
+// share a row (8 waves per SIMD spilled and ran 40 % slower); up to 7 steps in
+// 96 VGPRs (5) with one encode scale, in 128 (4) row-scaled; 8 steps in 128
+// or, row-scaled, 168 (3); wider rows get the whole register file.
+constexpr int split_waves(int nch, bool rowsc, int wpr) {
+    return nch <= 4 && wpr == 4 ? (rowsc ? 6 : 7)
+           : nch <= 7           ? (rowsc ? 4 : 5)
+           : nch == 8           ? (rowsc ? 3 : 4)
+                                : 1;
 }
 
-template <int FMT, bool ROWSC, int LAYOUT, int NCH2>
+template <int FMT, bool ROWSC, int LAYOUT, int NCH>
 __global__ __launch_bounds__(kSplitThreads)
-__attribute__((amdgpu_waves_per_eu(split_waves(NCH2, ROWSC))))
+__attribute__((amdgpu_waves_per_eu(split_waves(NCH, ROWSC, split_wpr(LAYOUT)))))
 void k_split(const SplitArgs a) {
     using Tr = FmtTraits<FMT>;
     constexpr bool kSwz = LAYOUT == MXQ_SF_SWIZZLED;
-    constexpr int kUnit = kSplitUnitRows;
-    constexpr int kPairs = kSplitThreads / 128;  // rows in flight: two waves per row
+    constexpr int kWpr = split_wpr(LAYOUT);      // waves per row
+    constexpr int kUnit = split_unit_rows(LAYOUT);  // rows per unit, all in flight at once
+    constexpr int kPairs = kUnit;
     extern __shared__ __align__(16) uint8_t stage[];  // the unit's codes, one row per sf_stride
     __shared__ uint32_t row_max[kUnit];  // one encode scale: row amax folded by LDS atomics
-    __shared__ uint32_t half_max[2][2 * kPairs];  // row-scaled: each wave's half-row amax, two buffers
+    __shared__ uint32_t half_max[2][kWpr * kPairs];  // row-scaled: each wave's part-row amax, two buffers
     __shared__ int64_t row_dst[kUnit];   // swizzled: offset of each row's piece of tile 0
     __shared__ int32_t row_zero[kUnit];  // swizzled: zero slots the row's store carries
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x >> 6;
-    const int pair = w >> 1, half = w & 1;
+    const int pair = w / kWpr, half = w % kWpr;  // the wave's row of the unit, its part of the row
     const bool leader = (lane & (Tr::kLanesPerBlock - 1)) == 0;
     const int64_t payload_ld = FMT == MXQ_MXFP8 ? a.cols : a.cols / 2;
     const float g = (FMT == MXQ_NVFP4 && !ROWSC) ? *a.g : 0.0f;
@@ -90,16 +103,17 @@ void k_split(const SplitArgs a) {
     int it = 0;  // row-scaled step counter, uniform over the workgroup
     for (int u0 = blockIdx.x; u0 < a.total_units; u0 += gridDim.x) {
         // swizzled: the padding units take the first dispatch slots, so their
-        // stores overlap the row units instead of trailing them; 32 consecutive
-        // row units (64 rows, whose codes fill the 16-byte lines of half a
-        // band) meet in one L2, which merges their partial-line stores
+        // stores overlap the row units instead of trailing them; the row
+        // units of 64 consecutive rows (whose codes fill the 16-byte lines of
+        // half a band, or share linear 128-byte lines) meet in one L2, which
+        // merges their partial-line stores
         int u = u0;
         if (kSwz) {
             const int pads = a.total_units - n_row_units;
             u = u0 < pads ? n_row_units + u0 : u0 - pads;
         }
         if (xcd_grouping_holds(gridDim.x, a.total_units) && u < n_row_units)
-            u = xcd_grouped_unit<32>(u, n_row_units);
+            u = xcd_grouped_unit<64 / kUnit>(u, n_row_units);
         if (kSwz && u >= n_row_units) {
             // padding unit of split s, whose last band has fewer than 32
             // live rows: the 16-byte chunks with no live row are zeroed
@@ -120,19 +134,19 @@ void k_split(const SplitArgs a) {
         auto load_row = [&](int j, u32x4 *v) {
             const uint16_t *src = a.src + (int64_t)(r0 + j) * a.cols;
 #pragma unroll
-            for (int k = 0; k < NCH2; ++k) {
-                const int col = (2 * k + half) * kChunk + lane * 8;
+            for (int k = 0; k < NCH; ++k) {
+                const int col = (kWpr * k + half) * kChunk + lane * 8;
                 v[k] = u32x4{0, 0, 0, 0};
                 if (col < a.cols)
                     v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + col));
             }
         };
-        u32x4 cur[NCH2];
+        u32x4 cur[NCH];
         // this wave's half-row amax (columns past the row were loaded as zeros)
         auto half_amax = [&]() {
             uint32_t am = 0;
 #pragma unroll
-            for (int k = 0; k < NCH2; ++k) am = max(am, amax_bits8(cur[k]));
+            for (int k = 0; k < NCH; ++k) am = max(am, amax_bits8(cur[k]));
             return wave_max(am);
         };
         // encode the half row in cur as row j of the unit under the encode
@@ -140,8 +154,8 @@ void k_split(const SplitArgs a) {
         auto encode = [&](int j, const NvG &Gr, uint32_t &am) {
             uint8_t *pay_row = a.payload + (int64_t)(r0 + j) * payload_ld;
 #pragma unroll
-            for (int k = 0; k < NCH2; ++k) {
-                const int col = (2 * k + half) * kChunk + lane * 8;
+            for (int k = 0; k < NCH; ++k) {
+                const int col = (kWpr * k + half) * kChunk + lane * 8;
                 u32x2 pay;
                 const uint32_t code = quant8<FMT>(cur[k], Gr, pay);
                 if (col < a.cols) {
@@ -198,7 +212,9 @@ void k_split(const SplitArgs a) {
                 if (lane == 0) half_max[it & 1][w] = am;
                 __syncthreads();
                 if (j < n_live) {
-                    const uint32_t ra = max(half_max[it & 1][2 * pair], half_max[it & 1][2 * pair + 1]);
+                    uint32_t ra = half_max[it & 1][kWpr * pair];
+#pragma unroll
+                    for (int p = 1; p < kWpr; ++p) ra = max(ra, half_max[it & 1][kWpr * pair + p]);
                     const float af = __uint_as_float(ra << 16);
                     const float gr = nv_encode_scale(af);
                     uint32_t unused = 0;
@@ -252,7 +268,7 @@ void k_split(const SplitArgs a) {
 template <int FMT, bool ROWSC, int LAYOUT>
 static void split_nch(const SplitArgs &a, dim3 gd, size_t lds, hipStream_t s) {
     const dim3 bd(kSplitThreads);
-    switch (half_row_steps(a.cols)) {
+    switch (split_steps(a.cols, split_wpr(LAYOUT))) {
     case 1: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 1>), gd, bd, lds, s, a); break;
     case 2: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 2>), gd, bd, lds, s, a); break;
     case 4: hipLaunchKernelGGL((k_split<FMT, ROWSC, LAYOUT, 4>), gd, bd, lds, s, a); break;
@@ -274,7 +290,7 @@ hipError_t launch_split(int fmt, bool row_scaled, int layout, const SplitArgs &a
                         hipStream_t s) {
     // the unit's codes; rounded up to 16 bytes, the granule of the zeroing
     // stores of the padding columns
-    const size_t lds = ((size_t)kSplitUnitRows * a.sf_stride + 15) & ~(size_t)15;
+    const size_t lds = ((size_t)split_unit_rows(layout) * a.sf_stride + 15) & ~(size_t)15;
     const dim3 gd((unsigned)(grid < 1 ? 1 : grid));
     if (fmt == MXQ_MXFP8)
         split_layout<MXQ_MXFP8, false>(layout, a, gd, lds, s);
