@@ -360,7 +360,10 @@ def main(argv=None):
             pay = T * (H if fmt == 0 else H // 2)
             alg = (T * H * 2 + pay + sum(sf_bytes(m, C, int(l)) for m in split) + 4 * T
                    + (4 if key == "nvfp4" else 0))
-            m = lambda n, g, f=f, rs=rs, l=l: f"k_split<{f}, {rs}, {l}, 7>" in n
+            # 512-column steps per wave at 7168 columns: 7 with two waves per row
+            # (swizzled), 4 with four (linear)
+            nch = 7 if l == "1" else 4
+            m = lambda n, g, f=f, rs=rs, l=l, nch=nch: f"k_split<{f}, {rs}, {l}, {nch}>" in n
             dur = [x[3] for x in select(trace, m)]
             n, fb, wb, ratio = pmc(m, alg)
             rows_s.append(f"| {key} | {LAY[l]} | {len(dur)} | {avg(dur) / 1e3:,.2f} | {alg:,} | "
@@ -374,7 +377,8 @@ def main(argv=None):
              "(10 empty, 19-55 rows each), MI355X",
              "Algorithmic bytes: bf16 input + payload + every expert's (padded) scale region + "
              "4 B of row amax per row.  8 input copies rotate (more than the 256 MB last-level "
-             "cache).\n\n" + calib + "\n"
+             "cache).  Linear scales: one-row units of four waves; swizzled: two-row units of "
+             "two waves per row.\n\n" + calib + "\n"
              "| form | scales | n | avg us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
              "|---|---|---|---|---|---|---|---|---|\n" + "\n".join(rows_s) + "\n")
 
