@@ -142,15 +142,16 @@ void k_split(const SplitArgs a) {
             }
         };
         u32x4 cur[NCH];
-        // this wave's half-row amax (columns past the row were loaded as zeros)
+        // the amax of this wave's part of the row (columns past the row were
+        // loaded as zeros)
         auto half_amax = [&]() {
             uint32_t am = 0;
 #pragma unroll
             for (int k = 0; k < NCH; ++k) am = max(am, amax_bits8(cur[k]));
             return wave_max(am);
         };
-        // encode the half row in cur as row j of the unit under the encode
-        // scale Gr; whole wave.  am accumulates the half row's amax bits.
+        // encode the wave's part of the row, in cur, as row j of the unit under
+        // the encode scale Gr; whole wave.  am accumulates the part's amax bits.
         auto encode = [&](int j, const NvG &Gr, uint32_t &am) {
             uint8_t *pay_row = a.payload + (int64_t)(r0 + j) * payload_ld;
 #pragma unroll
