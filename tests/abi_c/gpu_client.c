@@ -6,7 +6,8 @@
  * Covered: mx_quant_grouped (MXFP8 and NVFP4, linear and swizzled, ragged
  * rows, a strided source), the same entries through mx_quant_grouped_batch
  * (two launches, the second chained), nvfp4_quant_split_row_scaled (empty and ragged
- * experts, swizzled) and rmsnorm_quant_fused (MXFP8, swizzled).  Prints
+ * experts, swizzled) and rmsnorm_quant_fused (MXFP8, swizzled; 1, 3 and 20
+ * rows).  Prints
  * "ok: N checks" and exits 0 when everything matches. */
 #include <stdint.h>
 #include <stdio.h>
@@ -162,8 +163,8 @@ static void split_row_scaled(hipStream_t s) {
     HIP_OK(hipFree(d_x)); HIP_OK(hipFree(d_p)); HIP_OK(hipFree(d_s)); HIP_OK(hipFree(d_a));
 }
 
-static void fused(hipStream_t s) {
-    const int64_t T = 3, H = 256;
+static void fused(hipStream_t s, int64_t T) {
+    const int64_t H = 256;
     const int64_t sb = mxq_scale_bytes(T, H, MXQ_MXFP8, MXQ_SF_SWIZZLED);
     const size_t nb = (size_t)(T * H * 2);
     uint16_t *h_x = hmalloc(nb), *h_r = hmalloc(nb), *h_gm = hmalloc((size_t)H * 2);
@@ -224,9 +225,13 @@ int main(void) {
     printf("row-scaled split\n");
     fflush(stdout);
     split_row_scaled(s);
-    printf("fused epilogue\n");
-    fflush(stdout);
-    fused(s);
+    /* 1 and 20 rows run the one-workgroup-per-row kernel, 3 the general one */
+    const int64_t fused_rows[] = {1, 3, 20};
+    for (int i = 0; i < 3; ++i) {
+        printf("fused epilogue, %lld rows\n", (long long)fused_rows[i]);
+        fflush(stdout);
+        fused(s, fused_rows[i]);
+    }
     HIP_OK(hipStreamDestroy(s));
     printf("ok: %d checks, %d failed\n", checks, fails);
     return fails ? 1 : 0;
