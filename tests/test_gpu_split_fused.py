@@ -274,6 +274,17 @@ def test_fused_swizzled_partial_bands(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+def test_fused_few_rows_widths(orc, fmt):
+    """The one-workgroup-per-row kernel (T = 1 and 17..31, swizzled, H up to
+    16 x 512) at row widths of one tile, a partial last wave step (640, 2176),
+    and exactly sixteen full steps (8192); 8320 runs the general kernel."""
+    for T in (1, 20):
+        for H in (128, 640, 2176, 8192, 8320):
+            say("fused few rows, fmt", fmt, "T", T, "H", H)
+            _fused_check(orc, T, H, fmt, mxq.SWIZZLED, seed=T * 7 + H)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_fused_grid_invariance(orc, fmt):
     try:
         for T in (100, 2100):
