@@ -100,6 +100,14 @@ def hi(v):
     return max(v) if v else float("nan")
 
 
+def pct(v, q):
+    """The q-quantile of v (nearest rank), NaN when empty."""
+    if not v:
+        return float("nan")
+    w = sorted(v)
+    return w[min(len(w) - 1, int(q * len(w)))]
+
+
 CMD_VALU = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc VALUBusy --output-format csv "
             "-d $OUT/pmc_valu -o v -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-extra "
             "--no-cpu-baseline")
@@ -409,7 +417,8 @@ def main(argv=None):
                     return rows[k * per:(k + 1) * per]
                 dur = [x[3] for x in nth(select(trace, m))]
                 n, fb, wb, ratio = pmc(m, alg, nth)
-                rows_f.append(f"| {FMT[f]} | {Tt} | {len(dur)} | {avg(dur) / 1e3:,.2f} | {alg:,} | "
+                rows_f.append(f"| {FMT[f]} | {Tt} | {len(dur)} | {avg(dur) / 1e3:,.2f} | "
+                              f"{pct(dur, 0.5) / 1e3:,.2f} | {pct(dur, 0.1) / 1e3:,.2f} | {alg:,} | "
                               f"{alg / avg(dur):,.0f} | {fb:,.0f} | {wb:,.0f} | {ratio:.4f} |")
                 if Tt == 4096:
                     out["kernels"][f"k_fused<{FMT[f]},SWIZZLED>"] = {
@@ -429,8 +438,11 @@ def main(argv=None):
              "T as replays of a captured graph of 8 calls (a decode step runs the epilogue "
              "inside a graph; called one at a time from Python, the host's cost per call "
              "exceeds the kernel's and the GPU idles between launches).\n\n" + calib + "\n"
-             "| format | T | n | avg us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
-             "|---|---|---|---|---|---|---|---|---|\n" + "\n".join(rows_f) + "\n")
+             "Durations at small T are bimodal from launch to launch (medians of 3.9 or 4.7 us "
+             "at T = 16 in different runs), so the median and the 10th percentile stand beside "
+             "the mean; GB/s is over the mean.\n\n"
+             "| format | T | n | avg us | median us | p10 us | algorithmic B | GB/s | fetch B | write B | traffic / algorithmic |\n"
+             "|---|---|---|---|---|---|---|---|---|---|---|\n" + "\n".join(rows_f) + "\n")
 
     # ------------------------------------------------------------ swizzle
     rs_, cs_ = 16 * 3072, 128
